@@ -1,0 +1,273 @@
+"""Plain float64 oracle of ReHyAt hybrid attention (test infrastructure only).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg; never by the library. Shares no code with the HIP path.
+
+Source: the papernotes.org note "ReHyAt: Recurrent Hybrid Attention for Video Diffusion
+Transformers" (CVPR 2026), section "method details", key designs 1, 2 and 4. Notation:
+
+  N  = T*HW tokens, time-major (token f*HW + s is spatial position s of frame f);
+  N' = Tc*HW tokens per chunk; the queries of chunk t are rows [t*N', min((t+1)*N', N)).
+  Softmax key set of chunk t (key design 2, overlapped set):
+        S_t = [lo_t, hi_t),  lo_t = max(t*N' - To*HW, 0),  hi_t = min((t+1)*N', N).
+  Linear key set (key design 4, causal):          L_t = [0, lo_t)
+               (key design 1, bidirectional):     L_t = [0, lo_t) U [hi_t, N)
+                                                  (the complement of the overlapped window).
+  Branches (key design 1):  a^S = sum_{j in S_t} exp(q.k_j/sqrt(D)) v_j,  n^S = sum exp(.)
+                            a^L = sum_{j in L_t} (phi(q).phi(k_j)) v_j,   n^L = sum phi.phi
+  Joint normalisation (key design 1):  y = (a^S + a^L) / (n^S + n^L).
+  Feature map used throughout: phi(x)_i = 1 + u_i + u_i^2/2 with u = x W / sqrt(D),
+  W a D x F matrix (x a row vector). It is strictly positive: 1+u+u^2/2 = ((1+u)^2+1)/2 >= 1/2.
+
+Readings where the page is silent or inconsistent (each is also listed with its reason in
+the design notes of the repository):
+  * The softmax stabiliser c_t of key design 1 sits in the softmax branch only, so under the
+    joint normalisation it is not result-neutral; the oracle uses the unstabilised form
+    (c_t = 0). Any running max used by an implementation must be compensated exactly.
+  * n^S and n^L are the sums of the branch weights (the denominators of the recurrence in
+    key design 4 are n^S + phi(q) z_t with z_t = sum phi(k_j)).
+  * The recurrence of key design 4 as printed adds the whole softmax set S_t to the state;
+    with To > 0 that counts the overlap frames in both branches, contradicting the causal
+    linear set. The oracle follows the sets: after chunk t the state holds exactly the keys
+    j < lo_{t+1}, i.e. s_{t+1} = s_t + sum over [lo_t, lo_{t+1}). For To = 0 this is the
+    printed recurrence.
+  * No mask inside a chunk: the softmax window is bidirectional, overlap frames included.
+  * A last chunk shorter than Tc frames (T not a multiple of Tc) keeps hi = N.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "chunk_layout", "phi", "hybrid_attention", "hybrid_attention_bh", "hybrid_recurrent",
+    "state_direct", "recurrent_init", "recurrent_step",
+]
+
+
+def chunk_layout(T: int, HW: int, Tc: int, To: int) -> List[Tuple[int, int, int, int]]:
+    """Per chunk t: (row_lo, row_hi, lo_t, hi_t).
+
+    Rows [row_lo, row_hi) are the queries of chunk t (queries are not overlapped, key
+    design 2); [lo_t, hi_t) is its overlapped softmax key set (key design 2).
+    """
+    if min(T, HW, Tc) <= 0 or To < 0:
+        raise ValueError("T, HW, Tc must be positive and To non-negative")
+    N = T * HW
+    Np = Tc * HW
+    out = []
+    t = 0
+    while t * Np < N:
+        row_lo = t * Np
+        row_hi = min((t + 1) * Np, N)
+        lo = max(t * Np - To * HW, 0)
+        hi = row_hi
+        out.append((row_lo, row_hi, lo, hi))
+        t += 1
+    return out
+
+
+def phi(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """phi(x) = 1 + u + u*u/2, u = x W / sqrt(D), rows of x mapped independently."""
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    D = x.shape[-1]
+    u = (x @ W) / math.sqrt(D)
+    return 1.0 + u + 0.5 * u * u
+
+
+def _linear_keys(lo: int, hi: int, N: int, causal: bool) -> np.ndarray:
+    """Key indices of the linear set: [0, lo) (causal, key design 4) or its union with
+    [hi, N) (bidirectional: complement of the overlapped window, key design 1)."""
+    if causal:
+        return np.arange(0, lo)
+    return np.concatenate([np.arange(0, lo), np.arange(hi, N)])
+
+
+def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool = True,
+                     rows: Optional[Sequence[int]] = None, block: int = 256,
+                     return_stats: bool = False):
+    """Hybrid attention of one (batch, head), by the definition, query by query.
+
+    q, k, v: [N, D]; Wq, Wk: [D, F]. For every query the explicit weights over all of its
+    keys are formed (exp over the softmax set, phi(q).phi(k) over the linear set) and the
+    joint normalisation is applied (key design 1). Queries are processed in blocks of
+    `block` rows only to bound memory; nothing else is reordered.
+
+    rows: optional subset of query rows (outputs for other rows are not computed).
+    Returns y [len(rows) or N, D] (float64); with return_stats also a dict of the per-row
+    numerator/denominator parts nS, nL.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, D = q.shape
+    if N % HW:
+        raise ValueError("N must be a multiple of HW")
+    T = N // HW
+    rows_arr = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.empty((rows_arr.size, v.shape[1]), dtype=np.float64)
+    nS_out = np.empty(rows_arr.size)
+    nL_out = np.empty(rows_arr.size)
+    phik = phi(k, Wk)
+    inv_sqrt_d = 1.0 / math.sqrt(D)
+    for (row_lo, row_hi, lo, hi) in chunk_layout(T, HW, Tc, To):
+        sel = np.nonzero((rows_arr >= row_lo) & (rows_arr < row_hi))[0]
+        if sel.size == 0:
+            continue
+        Lidx = _linear_keys(lo, hi, N, causal)
+        kS, vS = k[lo:hi], v[lo:hi]
+        phikL, vL = phik[Lidx], v[Lidx]
+        for b0 in range(0, sel.size, block):
+            pos = sel[b0:b0 + block]
+            Qb = q[rows_arr[pos]]
+            ES = np.exp((Qb @ kS.T) * inv_sqrt_d)          # softmax branch weights, c_t = 0
+            num = ES @ vS
+            nS = ES.sum(axis=1)
+            if Lidx.size:
+                EL = phi(Qb, Wq) @ phikL.T                  # linear branch weights
+                num = num + EL @ vL
+                nL = EL.sum(axis=1)
+            else:
+                nL = np.zeros(pos.size)
+            y[pos] = num / (nS + nL)[:, None]
+            nS_out[pos] = nS
+            nL_out[pos] = nL
+    if return_stats:
+        return y, {"nS": nS_out, "nL": nL_out}
+    return y
+
+
+def _w_for_head(W: np.ndarray, h: int) -> np.ndarray:
+    W = np.asarray(W)
+    return W if W.ndim == 2 else W[h]
+
+
+def _one_head(args):
+    (q, k, v, Wq, Wk, HW, Tc, To, causal, rows, block) = args
+    return hybrid_attention(q, k, v, Wq, Wk, HW=HW, Tc=Tc, To=To, causal=causal,
+                            rows=rows, block=block)
+
+
+def hybrid_attention_bh(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool = True,
+                        rows: Optional[Sequence[int]] = None, block: int = 256,
+                        processes: int = 1, heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """hybrid_attention over [B, H, N, D] inputs; W is [D, F] (shared) or [H, D, F].
+
+    heads: optional list of (b, h) pairs to evaluate (others are left as NaN).
+    processes > 1 evaluates heads in a process pool (one BLAS thread per process is the
+    caller's business: set OMP_NUM_THREADS / OPENBLAS_NUM_THREADS before numpy loads).
+    Returns y [B, H, len(rows) or N, Dv].
+    """
+    B, H, N, _ = q.shape
+    nrows = N if rows is None else len(rows)
+    y = np.full((B, H, nrows, v.shape[-1]), np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    jobs = [(q[b, h], k[b, h], v[b, h], _w_for_head(Wq, h), _w_for_head(Wk, h),
+             HW, Tc, To, causal, rows, block) for (b, h) in pairs]
+    if processes > 1 and len(jobs) > 1:
+        import multiprocessing as mp
+        ctx = mp.get_context("fork")
+        with ctx.Pool(processes) as pool:
+            outs = pool.map(_one_head, jobs)
+    else:
+        outs = [_one_head(j) for j in jobs]
+    for (b, h), o in zip(pairs, outs):
+        y[b, h] = o
+    return y
+
+
+def state_direct(k, v, Wk, j_end: int, j_begin: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Recurrent state by its definition (key design 4): the direct sums over keys
+    j in [j_begin, j_end) of phi(k_j) v_j^T (an F x D matrix s) and phi(k_j) (z, length F)."""
+    k = np.asarray(k, dtype=np.float64)[j_begin:j_end]
+    v = np.asarray(v, dtype=np.float64)[j_begin:j_end]
+    pk = phi(k, Wk)
+    return pk.T @ v, pk.sum(axis=0)
+
+
+def hybrid_recurrent(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int,
+                     return_states: bool = False):
+    """Causal hybrid attention as the chunk-wise RNN of key design 4.
+
+    For chunk t:  y_t = (a^S_t + phi(Q_t) s_t) / (n^S_t + phi(Q_t) z_t), with s_t, z_t the
+    state carried from earlier chunks; then the state absorbs the keys that leave reach of
+    every later softmax window: s_{t+1} = s_t + sum_{j in [lo_t, lo_{t+1})} phi(k_j) v_j^T
+    (and z likewise), so that s_t always equals the sum over the causal linear set
+    [0, lo_t). This is an algorithm different from hybrid_attention (state hoisted out of
+    the query, sums carried across chunks); the two must agree.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, D = q.shape
+    T = N // HW
+    layout = chunk_layout(T, HW, Tc, To)
+    F = np.asarray(Wq).shape[1]
+    s = np.zeros((F, v.shape[1]))
+    z = np.zeros(F)
+    y = np.empty((N, v.shape[1]))
+    states = []
+    inv_sqrt_d = 1.0 / math.sqrt(D)
+    for t, (row_lo, row_hi, lo, hi) in enumerate(layout):
+        states.append((s.copy(), z.copy()))
+        Q = q[row_lo:row_hi]
+        ES = np.exp((Q @ k[lo:hi].T) * inv_sqrt_d)
+        aS = ES @ v[lo:hi]
+        nS = ES.sum(axis=1)
+        pq = phi(Q, Wq)
+        y[row_lo:row_hi] = (aS + pq @ s) / (nS + pq @ z)[:, None]
+        lo_next = layout[t + 1][2] if t + 1 < len(layout) else lo
+        if lo_next > lo:
+            pk = phi(k[lo:lo_next], Wk)
+            s = s + pk.T @ v[lo:lo_next]
+            z = z + pk.sum(axis=0)
+    if return_states:
+        return y, states
+    return y
+
+
+# ---------------------------------------------------------------------------------------
+# Streaming (one call per chunk), the sampling-time use of the RNN form (key design 4 and
+# the framework overview: one chunk of Tc frames generated at a time, state carried).
+#
+# Carried state after the chunks covering frames [0, f_end):
+#   S = sum over keys of frames [0, f_end - To) of phi(k) v^T,  z likewise,
+#   tail = the K and V rows of frames [f_end - To, f_end) (the overlap frames the next
+#          chunk's softmax window reaches back to; not named on the page, it follows from
+#          the overlapped softmax set and the causal linear set).
+# ---------------------------------------------------------------------------------------
+
+def recurrent_init(F: int, D: int) -> Dict[str, object]:
+    """Empty streaming state (before chunk 0)."""
+    return {"S": np.zeros((F, D)), "z": np.zeros(F), "k_tail": np.zeros((0, D)),
+            "v_tail": np.zeros((0, D)), "t": 0}
+
+
+def recurrent_step(state: Dict[str, object], q_c, k_c, v_c, Wq, Wk, *, HW: int, To: int):
+    """One chunk of the streaming form.
+
+    q_c, k_c, v_c: the chunk's rows [n_c, D] (n_c a multiple of HW). The softmax window is
+    tail + chunk (the overlapped set of key design 2), the linear part is read from the
+    state (key design 4). Returns (y_c, new_state); the input state is not modified.
+    """
+    q_c = np.asarray(q_c, dtype=np.float64)
+    k_c = np.asarray(k_c, dtype=np.float64)
+    v_c = np.asarray(v_c, dtype=np.float64)
+    D = q_c.shape[1]
+    S, z = state["S"], state["z"]
+    kw = np.concatenate([state["k_tail"], k_c])
+    vw = np.concatenate([state["v_tail"], v_c])
+    ES = np.exp((q_c @ kw.T) / math.sqrt(D))
+    pq = phi(q_c, Wq)
+    y = (ES @ vw + pq @ S) / (ES.sum(axis=1) + pq @ z)[:, None]
+    # Keys of the window that no later window reaches: all but the last To frames.
+    n_keep = min(To * HW, kw.shape[0])
+    n_fold = kw.shape[0] - n_keep
+    pk = phi(kw[:n_fold], Wk)
+    new = {"S": S + pk.T @ vw[:n_fold], "z": z + pk.sum(axis=0),
+           "k_tail": kw[n_fold:].copy(), "v_tail": vw[n_fold:].copy(),
+           "t": int(state["t"]) + 1}
+    return y, new
