@@ -1,0 +1,437 @@
+// api.cpp - the librehyat C ABI (include/rehyat.h): argument checks, workspace layout and
+// kernel orchestration on the caller's stream. Host code only; kernels live in *.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/rehyat.h"
+#include "common.h"
+
+namespace rehyat {
+hipError_t launch_attn_bf16(const AttnArgs& a, int F, hipStream_t stream);
+int attn_bf16_tile_rows();
+hipError_t launch_attn_f32(const AttnArgs& a, int D, int F, hipStream_t stream);
+int attn_f32_tile_rows();
+hipError_t launch_state_partial_bf16(const StateArgs& a, int F, int BH, hipStream_t stream);
+hipError_t launch_state_partial_f32(const StateArgs& a, int D, int F, int BH, hipStream_t stream);
+hipError_t launch_phi_bf16(const void* x, int64_t n, const void* W, int w_per_head, int H, int BH,
+                           int F, void* out, int out_f32, float u_scale, hipStream_t stream);
+hipError_t launch_phi_f32(const void* x, int64_t n, const void* W, int w_per_head, int H, int BH,
+                          int D, int F, void* out, float u_scale, hipStream_t stream);
+hipError_t launch_scan_states(const float* part, float* states, int F, int D, int T, int Tc,
+                              int To, int nch, int bidir, int BH, hipStream_t stream);
+hipError_t launch_fold_states(const float* part, int nseg, float* S, float* z, int F, int D,
+                              int init, int BH, hipStream_t stream);
+hipError_t launch_copy_rows(const void* sk, const void* sv, void* dk, void* dv, int64_t src_rows,
+                            int64_t src_row0, int64_t rows, int row_bytes, int BH,
+                            hipStream_t stream);
+}  // namespace rehyat
+
+using namespace rehyat;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rehyat_status fail(rehyat_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rehyat_status ok() {
+  g_err[0] = '\0';
+  return REHYAT_OK;
+}
+
+rehyat_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(REHYAT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t esize(int dtype) { return dtype == REHYAT_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+// Checks shared by every entry point.
+rehyat_status check_desc(const rehyat_desc* d) {
+  if (!d) return fail(REHYAT_ERR_NULL, "desc is NULL");
+  if (d->dtype != REHYAT_F32 && d->dtype != REHYAT_BF16)
+    return fail(REHYAT_ERR_DTYPE, "dtype %d unknown", d->dtype);
+  if (d->y_dtype != REHYAT_F32 && d->y_dtype != REHYAT_BF16)
+    return fail(REHYAT_ERR_DTYPE, "y_dtype %d unknown", d->y_dtype);
+  if (d->mode != REHYAT_CAUSAL && d->mode != REHYAT_BIDIR)
+    return fail(REHYAT_ERR_DTYPE, "mode %d unknown", d->mode);
+  if (d->w_per_head != 0 && d->w_per_head != 1)
+    return fail(REHYAT_ERR_SHAPE, "w_per_head must be 0 or 1");
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->HW < 1 || d->Tc < 1 || d->To < 0 || d->D < 1 ||
+      d->F < 1)
+    return fail(REHYAT_ERR_SHAPE, "B, H, T, HW, Tc, D, F must be >= 1 and To >= 0");
+  if (d->dtype == REHYAT_BF16) {
+    if (d->D != 128) return fail(REHYAT_ERR_UNSUPPORTED, "bf16 path supports D = 128 (got %d)", d->D);
+    if (d->F != 64 && d->F != 128 && d->F != 256)
+      return fail(REHYAT_ERR_UNSUPPORTED, "bf16 path supports F in {64,128,256} (got %d)", d->F);
+  } else {
+    if (d->D != 64 && d->D != 128)
+      return fail(REHYAT_ERR_UNSUPPORTED, "fp32 path supports D in {64,128} (got %d)", d->D);
+    if (d->F % 16 != 0 || d->F > 256)
+      return fail(REHYAT_ERR_UNSUPPORTED, "fp32 path supports F = 16..256, multiple of 16 (got %d)", d->F);
+  }
+  const int64_t N = (int64_t)d->T * d->HW;
+  const int64_t BH = (int64_t)d->B * d->H;
+  const int64_t width = d->D > d->F ? d->D : d->F;
+  if (BH * N * width >= kMaxElems) return fail(REHYAT_ERR_SHAPE, "tensor too large (>= 2^31 elements)");
+  if ((int64_t)d->Tc * d->HW >= kMaxElems / 256) return fail(REHYAT_ERR_SHAPE, "chunk too large");
+  return REHYAT_OK;
+}
+
+int n_chunks(const rehyat_desc* d) { return (d->T + d->Tc - 1) / d->Tc; }
+
+size_t state_elems(const rehyat_desc* d) { return (size_t)d->F * d->D + d->F; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// ---- kernel timing ----------------------------------------------------------------------
+constexpr int kMaxTimed = 4096;
+struct Timing {
+  bool enabled = false;
+  bool created = false;
+  int count = 0;
+  hipEvent_t ev[2 * kMaxTimed];
+};
+Timing g_timing;
+
+void timed_begin(hipStream_t s) {
+  if (g_timing.enabled && g_timing.count < kMaxTimed)
+    (void)hipEventRecord(g_timing.ev[2 * g_timing.count], s);
+}
+void timed_end(hipStream_t s) {
+  if (g_timing.enabled && g_timing.count < kMaxTimed) {
+    (void)hipEventRecord(g_timing.ev[2 * g_timing.count + 1], s);
+    g_timing.count++;
+  }
+}
+
+hipError_t launch_attention(const rehyat_desc* d, AttnArgs& a, hipStream_t s) {
+  timed_begin(s);
+  hipError_t e = (d->dtype == REHYAT_BF16) ? launch_attn_bf16(a, d->F, s)
+                                           : launch_attn_f32(a, d->D, d->F, s);
+  timed_end(s);
+  return e;
+}
+
+hipError_t launch_partial(const rehyat_desc* d, const StateArgs& sa, hipStream_t s) {
+  const int BH = d->B * d->H;
+  return (d->dtype == REHYAT_BF16) ? launch_state_partial_bf16(sa, d->F, BH, s)
+                                   : launch_state_partial_f32(sa, d->D, d->F, BH, s);
+}
+
+void fill_tiles(AttnArgs& a, const rehyat_desc* d, int nch_launch, int last_rows) {
+  const int QT = (d->dtype == REHYAT_BF16) ? attn_bf16_tile_rows() : attn_f32_tile_rows();
+  const int Np = d->Tc * d->HW;
+  a.tiles_per_chunk = (Np + QT - 1) / QT;
+  a.tiles_last = (last_rows + QT - 1) / QT;
+  a.tiles_per_head = (nch_launch - 1) * a.tiles_per_chunk + a.tiles_last;
+  a.nblocks = d->B * d->H * a.tiles_per_head;
+}
+
+constexpr int kStateSegRows = 512;   // rows per segment for rehyat_state_update
+
+}  // namespace
+
+extern "C" {
+
+const char* rehyat_status_str(rehyat_status s) {
+  switch (s) {
+    case REHYAT_OK: return "REHYAT_OK";
+    case REHYAT_ERR_NULL: return "REHYAT_ERR_NULL";
+    case REHYAT_ERR_SHAPE: return "REHYAT_ERR_SHAPE";
+    case REHYAT_ERR_DTYPE: return "REHYAT_ERR_DTYPE";
+    case REHYAT_ERR_ALIGN: return "REHYAT_ERR_ALIGN";
+    case REHYAT_ERR_UNSUPPORTED: return "REHYAT_ERR_UNSUPPORTED";
+    case REHYAT_ERR_WORKSPACE: return "REHYAT_ERR_WORKSPACE";
+    case REHYAT_ERR_HIP: return "REHYAT_ERR_HIP";
+    case REHYAT_ERR_ALIAS: return "REHYAT_ERR_ALIAS";
+  }
+  return "REHYAT_ERR_UNKNOWN";
+}
+
+const char* rehyat_last_error(void) { return g_err; }
+
+rehyat_status rehyat_phi(const rehyat_desc* d, const void* x, int64_t n, const void* W, void* phi,
+                         void* stream) {
+  rehyat_status st = check_desc(d);
+  if (st != REHYAT_OK) return st;
+  if (n < 0) return fail(REHYAT_ERR_SHAPE, "n < 0");
+  if (n == 0) return ok();
+  if (!x || !W || !phi) return fail(REHYAT_ERR_NULL, "x, W and phi must be non-NULL");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(phi))
+    return fail(REHYAT_ERR_ALIGN, "x, W, phi must be 16-byte aligned");
+  const int64_t BH = (int64_t)d->B * d->H;
+  if (BH * n * (d->D > d->F ? d->D : d->F) >= kMaxElems) return fail(REHYAT_ERR_SHAPE, "n too large");
+  const size_t es = esize(d->dtype);
+  if (overlaps(phi, BH * n * d->F * es, x, BH * n * d->D * es) ||
+      overlaps(phi, BH * n * d->F * es, W, (size_t)(d->w_per_head ? d->H : 1) * d->D * d->F * es))
+    return fail(REHYAT_ERR_ALIAS, "phi overlaps an input");
+  hipStream_t s = (hipStream_t)stream;
+  const float us = 1.0f / std::sqrt((float)d->D);
+  hipError_t e = (d->dtype == REHYAT_BF16)
+                     ? launch_phi_bf16(x, n, W, d->w_per_head, d->H, (int)BH, d->F, phi, 0, us, s)
+                     : launch_phi_f32(x, n, W, d->w_per_head, d->H, (int)BH, d->D, d->F, phi, us, s);
+  return hip_status(e, "rehyat_phi launch");
+}
+
+size_t rehyat_state_update_workspace(const rehyat_desc* d, int64_t n) {
+  if (check_desc(d) != REHYAT_OK || n <= 0) return 0;
+  const int64_t nseg = (n + kStateSegRows - 1) / kStateSegRows;
+  return (size_t)d->B * d->H * nseg * state_elems(d) * sizeof(float);
+}
+
+rehyat_status rehyat_state_update(const rehyat_desc* d, const void* k, const void* v, int64_t n,
+                                  const void* Wk, float* S, float* z, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  rehyat_status st = check_desc(d);
+  if (st != REHYAT_OK) return st;
+  if (n < 0) return fail(REHYAT_ERR_SHAPE, "n < 0");
+  if (n == 0) return ok();
+  if (!k || !v || !Wk || !S || !z) return fail(REHYAT_ERR_NULL, "k, v, Wk, S, z must be non-NULL");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(Wk) || !aligned16(S) || !aligned16(z))
+    return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+  const int64_t BH = (int64_t)d->B * d->H;
+  if (BH * n * d->D >= kMaxElems) return fail(REHYAT_ERR_SHAPE, "n too large");
+  const size_t need = rehyat_state_update_workspace(d, n);
+  if (!ws || ws_bytes < need)
+    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  const size_t es = esize(d->dtype);
+  const size_t nS = BH * d->F * d->D * sizeof(float), nz = BH * d->F * sizeof(float);
+  const size_t nkv = BH * n * d->D * es;
+  if (overlaps(S, nS, k, nkv) || overlaps(S, nS, v, nkv) || overlaps(z, nz, k, nkv) ||
+      overlaps(z, nz, v, nkv) || overlaps(S, nS, z, nz) || overlaps(ws, need, S, nS) ||
+      overlaps(ws, need, z, nz) || overlaps(ws, need, k, nkv) || overlaps(ws, need, v, nkv))
+    return fail(REHYAT_ERR_ALIAS, "S, z, workspace and inputs must not overlap");
+  StateArgs sa{};
+  sa.ka = k; sa.va = v; sa.a_rows = n; sa.a_row0 = 0;
+  sa.kb = k; sa.vb = v; sa.b_rows = n; sa.b_row0 = 0;
+  sa.na = n; sa.n = n;
+  sa.seg_len = kStateSegRows;
+  sa.n_seg = (int)((n + kStateSegRows - 1) / kStateSegRows);
+  sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
+  sa.part = reinterpret_cast<float*>(ws);
+  sa.u_scale = 1.0f / std::sqrt((float)d->D);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_partial(d, sa, s);
+  if (e != hipSuccess) return hip_status(e, "state partial launch");
+  e = launch_fold_states(sa.part, sa.n_seg, S, z, d->F, d->D, 0, (int)BH, s);
+  return hip_status(e, "state fold launch");
+}
+
+size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* d) {
+  if (check_desc(d) != REHYAT_OK) return 0;
+  const size_t BH = (size_t)d->B * d->H;
+  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float);
+}
+
+rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
+                                const void* Wq, const void* Wk, void* y, void* ws, size_t ws_bytes,
+                                void* stream) {
+  rehyat_status st = check_desc(d);
+  if (st != REHYAT_OK) return st;
+  if (!q || !k || !v || !Wq || !Wk || !y) return fail(REHYAT_ERR_NULL, "q, k, v, Wq, Wk, y must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(Wq) || !aligned16(Wk) ||
+      !aligned16(y))
+    return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+  const size_t need = rehyat_hybrid_fwd_workspace(d);
+  if (!ws || ws_bytes < need)
+    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  const int64_t N = (int64_t)d->T * d->HW;
+  const int BH = d->B * d->H;
+  const size_t es = esize(d->dtype);
+  const size_t nin = (size_t)BH * N * d->D * es, ny = (size_t)BH * N * d->D * esize(d->y_dtype);
+  const size_t nw = (size_t)(d->w_per_head ? d->H : 1) * d->D * d->F * es;
+  if (overlaps(y, ny, q, nin) || overlaps(y, ny, k, nin) || overlaps(y, ny, v, nin) ||
+      overlaps(y, ny, Wq, nw) || overlaps(y, ny, Wk, nw) || overlaps(ws, need, y, ny) ||
+      overlaps(ws, need, q, nin) || overlaps(ws, need, k, nin) || overlaps(ws, need, v, nin))
+    return fail(REHYAT_ERR_ALIAS, "y, workspace and inputs must not overlap");
+
+  hipStream_t s = (hipStream_t)stream;
+  const int nch = n_chunks(d);
+  const size_t E = state_elems(d);
+  float* part = reinterpret_cast<float*>(ws);              // [BH][T][E]
+  float* states = part + (size_t)BH * d->T * E;             // [BH][nch][E]
+  const float us = 1.0f / std::sqrt((float)d->D);
+  const bool need_state = nch > 1;   // a single chunk has an empty linear set in both modes
+
+  if (need_state) {
+    StateArgs sa{};
+    sa.ka = k; sa.va = v; sa.a_rows = N; sa.a_row0 = 0;
+    sa.kb = k; sa.vb = v; sa.b_rows = N; sa.b_row0 = 0;
+    sa.na = N; sa.n = N;
+    sa.seg_len = d->HW;
+    sa.n_seg = d->T;
+    sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
+    sa.part = part;
+    sa.u_scale = us;
+    hipError_t e = launch_partial(d, sa, s);
+    if (e != hipSuccess) return hip_status(e, "state partial launch");
+    e = launch_scan_states(part, states, d->F, d->D, d->T, d->Tc, d->To, nch,
+                           d->mode == REHYAT_BIDIR, BH, s);
+    if (e != hipSuccess) return hip_status(e, "state scan launch");
+  }
+
+  AttnArgs a{};
+  a.q = q; a.q_rows = N; a.y = y;
+  a.ka = k; a.va = v; a.a_rows = N;
+  a.kb = k; a.vb = v; a.b_rows = N;
+  a.Wq = Wq; a.w_per_head = d->w_per_head;
+  a.S = states; a.z = states + (size_t)d->F * d->D;
+  a.s_bh = (int64_t)nch * E; a.s_t = (int64_t)E; a.z_bh = a.s_bh; a.z_t = a.s_t;
+  a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
+  a.n_chunks = nch; a.chunk0 = 0; a.step = 0;
+  a.bidir = d->mode == REHYAT_BIDIR;
+  a.y_f32 = d->y_dtype == REHYAT_F32;
+  const int64_t Np = (int64_t)d->Tc * d->HW;
+  fill_tiles(a, d, nch, (int)(N - (int64_t)(nch - 1) * Np));
+  a.logit_scale = kLog2e / std::sqrt((float)d->D);
+  a.u_scale = us;
+  return hip_status(launch_attention(d, a, s), "attention launch");
+}
+
+size_t rehyat_recurrent_step_workspace(const rehyat_desc* d) {
+  if (check_desc(d) != REHYAT_OK) return 0;
+  return (size_t)d->B * d->H * d->Tc * state_elems(d) * sizeof(float);
+}
+
+rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void* q_c,
+                                    const void* k_c, const void* v_c, const void* Wq,
+                                    const void* Wk, float* S, float* z, void* k_tail, void* v_tail,
+                                    void* y_c, void* ws, size_t ws_bytes, void* stream) {
+  rehyat_status st = check_desc(d);
+  if (st != REHYAT_OK) return st;
+  if (d->To > d->Tc) return fail(REHYAT_ERR_UNSUPPORTED, "recurrent step needs To <= Tc");
+  const int nch = n_chunks(d);
+  if (t < 0 || t >= nch) return fail(REHYAT_ERR_SHAPE, "chunk_index %d outside [0, %d)", t, nch);
+  const int cf = (d->T - t * d->Tc) < d->Tc ? (d->T - t * d->Tc) : d->Tc;   // frames in chunk
+  if (cf < d->To) return fail(REHYAT_ERR_UNSUPPORTED, "final chunk of %d frames is shorter than To = %d", cf, d->To);
+  if (!q_c || !k_c || !v_c || !Wq || !Wk || !S || !z || !y_c)
+    return fail(REHYAT_ERR_NULL, "q_c, k_c, v_c, Wq, Wk, S, z, y_c must be non-NULL");
+  if (d->To > 0 && (!k_tail || !v_tail)) return fail(REHYAT_ERR_NULL, "k_tail, v_tail needed when To > 0");
+  if (!aligned16(q_c) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(Wq) || !aligned16(Wk) ||
+      !aligned16(S) || !aligned16(z) || !aligned16(y_c) ||
+      (d->To > 0 && (!aligned16(k_tail) || !aligned16(v_tail))))
+    return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+  const size_t need = rehyat_recurrent_step_workspace(d);
+  if (!ws || ws_bytes < need)
+    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  const int BH = d->B * d->H;
+  const int64_t crow = (int64_t)cf * d->HW;          // rows in this chunk
+  const int64_t trow = (int64_t)d->To * d->HW;       // rows in the tail
+  const size_t es = esize(d->dtype);
+  const size_t nc = (size_t)BH * crow * d->D * es, nt = (size_t)BH * trow * d->D * es;
+  const size_t ny = (size_t)BH * crow * d->D * esize(d->y_dtype);
+  const size_t nS = (size_t)BH * d->F * d->D * 4, nz = (size_t)BH * d->F * 4;
+  const void* ins[3] = {q_c, k_c, v_c};
+  for (const void* p : ins) {
+    if (overlaps(y_c, ny, p, nc) || overlaps(S, nS, p, nc) || overlaps(z, nz, p, nc) ||
+        overlaps(k_tail, nt, p, nc) || overlaps(v_tail, nt, p, nc) || overlaps(ws, need, p, nc))
+      return fail(REHYAT_ERR_ALIAS, "outputs must not overlap the chunk inputs");
+  }
+  if (overlaps(S, nS, z, nz) || overlaps(y_c, ny, S, nS) || overlaps(y_c, ny, z, nz) ||
+      overlaps(k_tail, nt, v_tail, nt) || overlaps(y_c, ny, k_tail, nt) ||
+      overlaps(y_c, ny, v_tail, nt) || overlaps(ws, need, S, nS) || overlaps(ws, need, z, nz) ||
+      overlaps(ws, need, y_c, ny) || overlaps(ws, need, k_tail, nt) || overlaps(ws, need, v_tail, nt))
+    return fail(REHYAT_ERR_ALIAS, "outputs and workspace must not overlap");
+
+  hipStream_t s = (hipStream_t)stream;
+  const float us = 1.0f / std::sqrt((float)d->D);
+  const int64_t tail_in = (t > 0) ? trow : 0;        // tail rows in the window
+
+  // 1. attention over window = tail + chunk, linear branch from the carried state
+  AttnArgs a{};
+  a.q = q_c; a.q_rows = crow; a.y = y_c;
+  a.ka = k_tail ? k_tail : k_c; a.va = v_tail ? v_tail : v_c; a.a_rows = k_tail ? trow : crow;
+  a.kb = k_c; a.vb = v_c; a.b_rows = crow;
+  a.Wq = Wq; a.w_per_head = d->w_per_head;
+  a.S = S; a.z = z;
+  a.s_bh = (int64_t)d->F * d->D; a.s_t = 0; a.z_bh = d->F; a.z_t = 0;
+  a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
+  a.n_chunks = 1; a.chunk0 = t; a.step = 1; a.bidir = 0;
+  a.y_f32 = d->y_dtype == REHYAT_F32;
+  fill_tiles(a, d, 1, (int)crow);
+  a.logit_scale = kLog2e / std::sqrt((float)d->D);
+  a.u_scale = us;
+  hipError_t e = launch_attention(d, a, s);
+  if (e != hipSuccess) return hip_status(e, "attention launch");
+
+  // 2. fold the window rows that no later window reaches (all but the last To frames)
+  const int64_t nfold = tail_in + crow - trow;
+  float* part = reinterpret_cast<float*>(ws);
+  if (nfold > 0) {
+    StateArgs sa{};
+    sa.ka = a.ka; sa.va = a.va; sa.a_rows = a.a_rows; sa.a_row0 = 0;
+    sa.kb = k_c; sa.vb = v_c; sa.b_rows = crow; sa.b_row0 = 0;
+    sa.na = tail_in; sa.n = nfold;
+    sa.seg_len = d->HW;
+    sa.n_seg = (int)((nfold + d->HW - 1) / d->HW);
+    sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
+    sa.part = part;
+    sa.u_scale = us;
+    e = launch_partial(d, sa, s);
+    if (e != hipSuccess) return hip_status(e, "state partial launch");
+    e = launch_fold_states(part, sa.n_seg, S, z, d->F, d->D, t == 0, BH, s);
+    if (e != hipSuccess) return hip_status(e, "state fold launch");
+  } else if (t == 0) {
+    e = launch_fold_states(part, 0, S, z, d->F, d->D, 1, BH, s);   // empty state
+    if (e != hipSuccess) return hip_status(e, "state init launch");
+  }
+
+  // 3. the chunk's last To frames become the tail
+  if (trow > 0) {
+    e = launch_copy_rows(k_c, v_c, k_tail, v_tail, crow, crow - trow, trow, (int)(d->D * es), BH, s);
+    if (e != hipSuccess) return hip_status(e, "tail copy launch");
+  }
+  return ok();
+}
+
+rehyat_status rehyat_timing_enable(int32_t enable) {
+  if (enable && !g_timing.created) {
+    for (int i = 0; i < 2 * kMaxTimed; ++i) {
+      hipError_t e = hipEventCreate(&g_timing.ev[i]);
+      if (e != hipSuccess) return hip_status(e, "hipEventCreate");
+    }
+    g_timing.created = true;
+  }
+  g_timing.enabled = enable != 0;
+  g_timing.count = 0;
+  return ok();
+}
+
+rehyat_status rehyat_timing_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(REHYAT_ERR_NULL, "outputs must be non-NULL");
+  *total_ms = 0.0;
+  *launches = g_timing.count;
+  if (g_timing.count > 0) {
+    hipError_t e = hipEventSynchronize(g_timing.ev[2 * g_timing.count - 1]);
+    if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
+    for (int i = 0; i < g_timing.count; ++i) {
+      float ms = 0.0f;
+      e = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
+      if (e != hipSuccess) return hip_status(e, "hipEventElapsedTime");
+      *total_ms += ms;
+    }
+  }
+  g_timing.count = 0;
+  return ok();
+}
+
+}  // extern "C"

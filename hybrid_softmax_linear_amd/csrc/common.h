@@ -1,0 +1,159 @@
+// common.h - device types, MFMA operand layouts and launch-argument structs shared by the
+// librehyat kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rehyat {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------------------
+// v_mfma_f32_32x32x16_bf16 operand layouts (wave64), lane l = 0..63:
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. 8*(l/32)+7
+//   B (16 x 32): lane l holds col l%32, k = 8*(l/32) .. 8*(l/32)+7
+//   C (32 x 32): lane l, element i holds row 8*(i/4) + 4*(l/32) + (i%4), col l%32
+// A C tile has lane = column, so a C tile of X^T (rows = contraction index of the next
+// product) can be fed straight back as the B operand of the next MFMA, and as the A
+// operand when the lane index is the A row. For that, the rows of the first product are
+// loaded in the order kappa(r) (bits 2 and 3 of r swapped): then C element i of lane l
+// carries contraction index cidx(i, l) = 16*(i/8) + 8*(l/32) + (i%8), so elements
+// 8j..8j+7 are exactly the k-slots of k-step j of a 32x32x16 operand, in natural order.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int kappa(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+__device__ __forceinline__ int cidx(int i, int lane) {
+  return 16 * (i >> 3) + 8 * (lane >> 5) + (i & 7);
+}
+// row of C element i of lane l (natural MFMA row, used for the output tiles)
+__device__ __forceinline__ int crow(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ u32x4 as_u32x4(const bf16x8& v) {
+  return __builtin_bit_cast(u32x4, v);
+}
+
+// Pack two floats into bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
+  bf16x2 r;
+  r[0] = (bf16)a;
+  r[1] = (bf16)b;
+  return r;
+}
+__device__ __forceinline__ unsigned pack_bf16_u32(float a, float b) {
+  return __builtin_bit_cast(unsigned, pack_bf16(a, b));
+}
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16 x) {
+  return __builtin_bit_cast(float, ((unsigned)__builtin_bit_cast(unsigned short, x)) << 16);
+}
+
+// Reductions over the lane pair (l, l^32) via v_permlane32_swap. With the same value x
+// in both operands the instruction returns p0 = {x[l] for l<32, x[l-32] for l>=32} and
+// p1 = {x[l+32] for l<32, x[l] for l>=32}: p0 and p1 hold the pair's two values in every
+// lane.
+__device__ __forceinline__ void pair_vals(float x, float& a, float& b) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  a = __builtin_bit_cast(float, (unsigned)p[0]);
+  b = __builtin_bit_cast(float, (unsigned)p[1]);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_vals(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_vals(x, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Wave-uniform "any lane true".
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8). Remap so that
+// consecutive logical tiles (which share K/V windows) land on the same XCD and its L2.
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+  const int nx = 8;
+  int q = nblocks / nx, r = nblocks % nx;
+  int x = b % nx, i = b / nx;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Offsets of a head inside [B, H, rows, cols] tensors use 64-bit arithmetic.
+__device__ __forceinline__ int64_t head_off(int bh, int64_t rows, int cols) {
+  return (int64_t)bh * rows * cols;
+}
+
+// ---------------------------------------------------------------------------------------
+// Launch arguments.
+// ---------------------------------------------------------------------------------------
+
+// Hybrid attention: one workgroup per (head, chunk, query tile).
+struct AttnArgs {
+  const void* q;        // query rows; head bh starts at q + bh*q_rows*D
+  int64_t q_rows;       // rows per head in the q / y buffers
+  void* y;              // output, same row layout as q
+  // Keys/values of a chunk's softmax window: window row w < na comes from segment A at row
+  // (a_row0 + w), otherwise from segment B at row (w - na). Per-head row counts give the
+  // head strides. For the whole-sequence form A is the sequence itself and nb = 0.
+  const void* ka; const void* va; int64_t a_rows;
+  const void* kb; const void* vb; int64_t b_rows;
+  const void* Wq;       // [D, F] or [H, D, F]
+  int w_per_head;
+  const float* S;       // linear state of (head, chunk): S + bh*s_bh + t*s_t, [F, D]
+  const float* z;       //                                 z + bh*z_bh + t*z_t, [F]
+  int64_t s_bh, s_t, z_bh, z_t;
+  int H;
+  int HW, Tc, To, T;    // geometry of the whole video
+  int n_chunks;         // chunks handled by this launch
+  int chunk0;           // index of the first chunk handled (step path: the chunk index)
+  int step;             // 1: window = tail (A) + chunk (B); 0: window inside the sequence
+  int bidir;
+  int y_f32;            // output dtype: 1 fp32, 0 bf16
+  int tiles_per_chunk;  // query tiles of a full chunk
+  int tiles_last;       // query tiles of the last chunk handled
+  int tiles_per_head;
+  int nblocks;
+  float logit_scale;    // log2(e) / sqrt(D)
+  float u_scale;        // 1 / sqrt(D)
+};
+
+// Per-segment partial states: one workgroup per (head, segment).
+struct StateArgs {
+  const void* ka; const void* va; int64_t a_rows; int64_t a_row0;  // rows [0, na) from A
+  const void* kb; const void* vb; int64_t b_rows; int64_t b_row0;  // then rows from B
+  int64_t na, n;        // rows in A, total rows
+  int seg_len;          // rows per segment
+  int n_seg;            // segments per head
+  const void* Wk; int w_per_head; int H;
+  float* part;          // [BH, n_seg, F*D + F] fp32 partial (S then z)
+  float u_scale;
+};
+
+}  // namespace rehyat

@@ -1,0 +1,110 @@
+// tiles_bf16.h - staging of 64-row K/V tiles (D = 128, bf16) through LDS, for workgroups of
+// 256 threads. Shared by the hybrid-attention and the state-reduction kernels.
+//
+// K tile : [64 keys][128 d], rows of 256 B. 16-byte chunk c of row r is stored at chunk
+//          c ^ kappa(r & 15). Readers take rows kappa(l%32) + 32*kb at chunk 2s + l/32, so
+//          each group of 16 lanes hits 16 distinct chunk columns (no bank conflicts).
+// V^T tile: [128 d][64 keys], rows of 128 B: the key index becomes the contiguous MFMA
+//          k-dimension. 8-key chunk kc of row d is stored at chunk kc ^ ((d + d/8) & 7):
+//          readers (rows d..d+7 at one chunk) and the transposing writers (16 rows at
+//          one key) both spread over the bank columns.
+#pragma once
+
+#include "common.h"
+
+namespace rehyat {
+
+constexpr int kTileRows = 64;
+constexpr int kDim = 128;
+constexpr int kKTileBytes = kTileRows * kDim * 2;   // 16 KB
+constexpr int kVTileBytes = kTileRows * kDim * 2;   // 16 KB
+
+__device__ __forceinline__ int ktile_off(int r, int c) {
+  return r * 256 + ((c ^ kappa(r & 15)) << 4);
+}
+__device__ __forceinline__ int vtile_off(int d, int key) {
+  return d * 128 + ((((key >> 3) ^ ((d + (d >> 3)) & 7))) << 4) + ((key & 7) << 1);
+}
+// 16-byte chunk kc (keys 8kc..8kc+7) of V^T row d
+__device__ __forceinline__ int vtile_chunk_off(int d, int kc) {
+  return d * 128 + ((kc ^ ((d + (d >> 3)) & 7)) << 4);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const unsigned char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// Rows of one tile come from up to two row segments of a [rows, 128] bf16 head:
+// tile row w (global window row w0 + w) is segment A row (a_row0 + w) if < na, else
+// segment B row (w - na). Rows at or beyond n are zero-filled.
+struct RowSrc {
+  const uint16_t* a;   // head base of segment A (already offset by the head)
+  const uint16_t* b;   // head base of segment B
+  int64_t a_row0;
+  int64_t na, n;
+};
+
+__device__ __forceinline__ const uint16_t* row_ptr(const RowSrc& s, int64_t w) {
+  return (w < s.na) ? s.a + (s.a_row0 + w) * kDim : s.b + (w - s.na) * kDim;
+}
+
+// Each of 256 threads loads 4 x 16 B of K and of V for tile rows [w0, w0+64).
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ void tile_load(TileRegs& r, const RowSrc& ks, const RowSrc& vs,
+                                          int64_t w0, int tid) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    int id = it * 256 + tid;
+    int row = id >> 4, c = id & 15;
+    int64_t w = w0 + row;
+    if (w < ks.n) {
+      r.k[it] = *reinterpret_cast<const u32x4*>(row_ptr(ks, w) + c * 8);
+      r.v[it] = *reinterpret_cast<const u32x4*>(row_ptr(vs, w) + c * 8);
+    } else {
+      r.k[it] = u32x4{0u, 0u, 0u, 0u};
+      r.v[it] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& r, unsigned char* kt,
+                                           unsigned char* vt, int tid) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    int id = it * 256 + tid;
+    int row = id >> 4, c = id & 15;
+    *reinterpret_cast<u32x4*>(kt + ktile_off(row, c)) = r.k[it];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      unsigned w = r.v[it][e >> 1];
+      uint16_t h = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+      *reinterpret_cast<uint16_t*>(vt + vtile_off(c * 8 + e, row)) = h;
+    }
+  }
+}
+
+// Stage W^T for features [f0, f0+nf) into LDS as [nf][128 d] rows of 256 B, in the K-tile
+// layout (row f, chunk c at c ^ kappa(f & 15)). W is [128 d][F] bf16 (row-major).
+__device__ __forceinline__ void stage_wt(unsigned char* dst, const uint16_t* W, int F, int f0,
+                                         int nf, int tid) {
+  // pairs (d, chunk of 8 features): thread reads W[d][f0 + 8c .. +8]
+  const int pairs = kDim * (nf / 8);
+  for (int id = tid; id < pairs; id += 256) {
+    int d = id & (kDim - 1), c = id >> 7;
+    u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)d * F + f0 + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      unsigned x = w[e >> 1];
+      uint16_t h = (e & 1) ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffffu);
+      int f = c * 8 + e;
+      *reinterpret_cast<uint16_t*>(dst + f * 256 + ((((d >> 3) ^ kappa(f & 15))) << 4) +
+                                   ((d & 7) << 1)) = h;
+    }
+  }
+}
+
+}  // namespace rehyat

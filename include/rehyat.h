@@ -1,0 +1,160 @@
+/*
+ * rehyat.h - C ABI of librehyat: ReHyAt temporally chunked hybrid attention on MI355X (gfx950).
+ *
+ * The method (papernotes.org note "ReHyAt: Recurrent Hybrid Attention for Video Diffusion
+ * Transformers", section "method details"):
+ *   - N = T*HW tokens, time-major: token f*HW + s is spatial position s of latent frame f.
+ *   - Chunks of Tc frames (N' = Tc*HW tokens). The queries of chunk t are the rows
+ *     [t*N', min((t+1)*N', N)) (key design 1).
+ *   - Softmax keys of chunk t: [lo_t, hi_t), lo_t = max(t*N' - To*HW, 0),
+ *     hi_t = min((t+1)*N', N): the chunk plus the To frames before it (key design 2).
+ *   - Linear keys: causal [0, lo_t) (key design 4); bidirectional [0, lo_t) U [hi_t, N),
+ *     the complement of the overlapped window (key design 1).
+ *   - y = (a^S + a^L) / (n^S + n^L) with a^S = sum_S exp(q.k/sqrt(D)) v,
+ *     a^L = phi(q) (sum_L phi(k) v^T), n^S, n^L the matching weight sums (key design 1).
+ *     No stabiliser enters the result: running maxima inside the kernels are compensated
+ *     exactly.
+ *   - Feature map: phi(x)_i = 1 + u_i + u_i^2/2, u = x W / sqrt(D), W a D x F matrix.
+ *   - Causal form as a chunk-wise RNN (key design 4): state S = sum phi(k) v^T (F x D) and
+ *     z = sum phi(k) (F) over the keys already out of reach of the softmax window.
+ *
+ * Conventions for every entry point
+ *   - All tensors are dense, row-major, head-major: [B, H, rows, cols]. Device pointers
+ *     must be 16-byte aligned. The caller owns every buffer; the library allocates no
+ *     device memory, keeps no state between calls and never synchronises the stream.
+ *   - dtype REHYAT_BF16: q, k, v, W (and tails) are bf16; products run on bf16 MFMA with
+ *     fp32 accumulation; phi(q), phi(k), the softmax weights and the state are rounded to
+ *     bf16 where they enter an MFMA. dtype REHYAT_F32: everything in fp32.
+ *     S and z are always fp32. y has dtype y_dtype (fp32 or bf16).
+ *   - `stream` is a hipStream_t (NULL: the null stream). Work is enqueued asynchronously.
+ *   - Argument checks run on the host before anything is enqueued; on failure nothing is
+ *     launched, outputs are untouched and a status != REHYAT_OK is returned (details in
+ *     rehyat_last_error()). No C++ exception crosses this boundary and nothing aborts.
+ *   - Outputs must not overlap inputs.
+ *   - Supported sizes: bf16: D = 128, F in {64, 128, 256}. fp32: D in {64, 128},
+ *     F in {16, 32, ..., 256} (a multiple of 16). B, H >= 1; T, HW, Tc >= 1; To >= 0;
+ *     B*H*T*HW*max(D,F) < 2^31 elements per tensor.
+ */
+#ifndef REHYAT_H
+#define REHYAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  REHYAT_OK = 0,
+  REHYAT_ERR_NULL = 1,        /* a required pointer is NULL */
+  REHYAT_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  REHYAT_ERR_DTYPE = 3,       /* unknown dtype or mode value */
+  REHYAT_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  REHYAT_ERR_UNSUPPORTED = 5, /* valid, but outside the supported sizes listed above */
+  REHYAT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace() size */
+  REHYAT_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
+  REHYAT_ERR_ALIAS = 8        /* an output overlaps an input */
+} rehyat_status;
+
+typedef enum { REHYAT_F32 = 0, REHYAT_BF16 = 1 } rehyat_dtype;
+typedef enum { REHYAT_CAUSAL = 0, REHYAT_BIDIR = 1 } rehyat_mode;
+
+/* Problem description shared by all entry points. */
+typedef struct {
+  int32_t B, H;       /* batch, heads */
+  int32_t T, HW;      /* latent frames of the whole video, tokens per frame (N = T*HW) */
+  int32_t D, F;       /* head dimension, feature dimension of phi */
+  int32_t Tc, To;     /* frames per chunk, overlap frames (softmax window reach-back) */
+  int32_t dtype;      /* rehyat_dtype of q, k, v, W, k_tail, v_tail */
+  int32_t y_dtype;    /* rehyat_dtype of y */
+  int32_t mode;       /* rehyat_mode (rehyat_hybrid_fwd only; the step path is causal) */
+  int32_t w_per_head; /* 0: Wq and Wk are [D, F] shared by all heads; 1: they are [H, D, F] */
+} rehyat_desc;
+
+/*
+ * Feature map phi (the fixed polynomial map above; the ReHyAt note's key design 3 uses a
+ * learned polynomial map in its place).
+ *   x   [B, H, n, D]  dtype     (device)
+ *   W   [D, F] or [H, D, F]     (device)
+ *   phi [B, H, n, F]  dtype     (device, written)
+ * n >= 0 rows per (b, h); n = 0 is a no-op.
+ */
+rehyat_status rehyat_phi(const rehyat_desc* desc, const void* x, int64_t n, const void* W,
+                         void* phi, void* stream);
+
+/*
+ * Recurrent-state update (key design 4, the sums s and z of the chunk-wise RNN):
+ *   S[b,h] += sum_{rows r} phi(k_r) v_r^T,   z[b,h] += sum_r phi(k_r)
+ *   k, v  [B, H, n, D]  dtype   (device)
+ *   Wk    [D, F] or [H, D, F]   (device)
+ *   S     [B, H, F, D]  fp32    (device, read and written)
+ *   z     [B, H, F]     fp32    (device, read and written)
+ *   ws    device scratch of at least rehyat_state_update_workspace(desc, n) bytes.
+ * The reduction order is fixed: results are bitwise reproducible.
+ */
+size_t rehyat_state_update_workspace(const rehyat_desc* desc, int64_t n);
+rehyat_status rehyat_state_update(const rehyat_desc* desc, const void* k, const void* v,
+                                  int64_t n, const void* Wk, float* S, float* z,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole-sequence hybrid attention (key designs 1, 2 and 4): causal (mode REHYAT_CAUSAL,
+ * the non-recursive form of the chunk-wise RNN) or bidirectional (REHYAT_BIDIR).
+ *   q, k, v [B, H, N, D] dtype  (device), N = T*HW; T need not be a multiple of Tc (the
+ *                                last chunk is then shorter)
+ *   Wq, Wk  [D, F] or [H, D, F] (device; may be the same buffer)
+ *   y       [B, H, N, D] y_dtype (device, written)
+ *   ws      device scratch of at least rehyat_hybrid_fwd_workspace(desc) bytes (per-frame
+ *           partial states and the per-chunk linear-branch states).
+ */
+size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* desc);
+rehyat_status rehyat_hybrid_fwd(const rehyat_desc* desc, const void* q, const void* k,
+                                const void* v, const void* Wq, const void* Wk, void* y,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One chunk of the causal form run as the chunk-wise RNN (key design 4), the sampling-time
+ * use in which one chunk of Tc frames is produced at a time with the state carried.
+ *   chunk_index t >= 0; the chunk holds frames [t*Tc, min((t+1)*Tc, T)), c_f of them.
+ *   q_c, k_c, v_c [B, H, c_f*HW, D] dtype (device)
+ *   S [B,H,F,D], z [B,H,F] fp32 (device, read and written): on entry the sums over all
+ *           keys before lo_t; on exit the sums over all keys before lo_{t+1}. For t = 0 the
+ *           entry values are ignored (the state starts empty).
+ *   k_tail, v_tail [B, H, To*HW, D] dtype (device, read and written): on entry the K and V
+ *           rows of the To frames before the chunk (ignored for t = 0); on exit those of
+ *           the chunk's last To frames. May be NULL when To = 0.
+ *   y_c  [B, H, c_f*HW, D] y_dtype (device, written)
+ *   ws   device scratch of at least rehyat_recurrent_step_workspace(desc) bytes.
+ * Requirements: To <= Tc; c_f >= To (a short final chunk must still cover the tail).
+ * Memory use is independent of t: calling it for t = 0, 1, 2, ... reproduces
+ * rehyat_hybrid_fwd(mode = REHYAT_CAUSAL) chunk by chunk (up to rounding order).
+ */
+size_t rehyat_recurrent_step_workspace(const rehyat_desc* desc);
+rehyat_status rehyat_recurrent_step(const rehyat_desc* desc, int32_t chunk_index,
+                                    const void* q_c, const void* k_c, const void* v_c,
+                                    const void* Wq, const void* Wk, float* S, float* z,
+                                    void* k_tail, void* v_tail, void* y_c,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* rehyat_status_str(rehyat_status status);
+
+/* Detail message of the last failed call on the calling host thread ("" if none). */
+const char* rehyat_last_error(void);
+
+/*
+ * Kernel timing (measurement aid). While enabled, every launch of the hybrid-attention
+ * kernel is bracketed by HIP events recorded on the launch stream (events are created
+ * once, at most 4096 launches are recorded). rehyat_timing_read synchronises on the last
+ * recorded event and returns the summed kernel time in milliseconds and the launch count,
+ * then clears the record. Enabling clears the record too. Not thread-safe.
+ */
+rehyat_status rehyat_timing_enable(int32_t enable);
+rehyat_status rehyat_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REHYAT_H */

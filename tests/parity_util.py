@@ -1,0 +1,79 @@
+"""Helpers shared by the GPU parity tests: oracle references on sampled rows, error
+summaries and the tolerance model.
+
+Tolerances
+  * fp32 path: max-abs error <= 1e-4 (the required bar for fp32).
+  * bf16 path: max-abs error <= 3e-2 (the required bar for bf16 inputs, fp32 accumulation).
+    Internal bar, derived from where the kernel rounds: the softmax weights p_j enter the
+    PV product as bf16 (relative error <= 2^-9 each), phi(q) and the state S enter the
+    linear read-out as bf16 (<= 2^-9 each). y is a weighted mean of values with positive
+    weights, and perturbing each weight by a factor (1+d_j), |d_j| <= 2^-9, moves a
+    weighted mean by at most 2^-9 * max_j |v_j - y| / (1 - 2^-9) <= 2^-8 * max|v| (both
+    numerator and denominator use the same rounded weights). The linear branch adds the
+    same order again. Hence |err| <= 2 * 2^-8 * max|v| (+ 2^-9 * max|y| when y is stored
+    as bf16). Typical errors are an order of magnitude below this bound; per-chunk errors
+    are reported by every test.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle as orc
+from synthetic import to_f64
+
+F32_BAR = 1e-4
+BF16_BAR = 3e-2
+
+
+def bf16_internal_bar(v: np.ndarray, y_ref: np.ndarray, y_bf16: bool) -> float:
+    bar = 2.0 * 2.0 ** -8 * float(np.abs(v).max())
+    if y_bf16:
+        bar += 2.0 ** -9 * float(np.abs(y_ref).max())
+    return bar
+
+
+def oracle_rows(inp: Dict[str, torch.Tensor], *, HW: int, Tc: int, To: int, causal: bool,
+                rows: Optional[Sequence[int]] = None,
+                heads: Optional[Iterable] = None) -> np.ndarray:
+    """Oracle output [B, H, len(rows) or N, D] (float64) on the stored inputs."""
+    q, k, v = to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"])
+    Wq = to_f64(inp["W"])
+    Wk = to_f64(inp["Wk"]) if "Wk" in inp else Wq
+    return orc.hybrid_attention_bh(q, k, v, Wq, Wk, HW=HW, Tc=Tc, To=To, causal=causal,
+                                   rows=rows, heads=heads)
+
+
+def sample_rows(T: int, HW: int, Tc: int, per_edge: int, n_random: int, seed: int = 0) -> List[int]:
+    """First and last `per_edge` query rows of every chunk, plus random rows."""
+    N, Np = T * HW, Tc * HW
+    rows = set()
+    for (r0, r1, _, _) in orc.chunk_layout(T, HW, Tc, 0):
+        rows.update(range(r0, min(r0 + per_edge, r1)))
+        rows.update(range(max(r1 - per_edge, r0), r1))
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, N, size=n_random).tolist())
+    return sorted(rows)
+
+
+def chunk_errors(y: np.ndarray, ref: np.ndarray, rows: Sequence[int], T: int, HW: int,
+                 Tc: int) -> List[Dict[str, float]]:
+    """Max-abs and RMS error per chunk (rows: the query row of each position on axis 2)."""
+    rows = np.asarray(rows)
+    out = []
+    for t, (r0, r1, _, _) in enumerate(orc.chunk_layout(T, HW, Tc, 0)):
+        sel = (rows >= r0) & (rows < r1)
+        if not sel.any():
+            continue
+        e = np.abs(y[:, :, sel] - ref[:, :, sel])
+        out.append({"chunk": t, "max_abs": float(e.max()), "rms": float(np.sqrt((e ** 2).mean())),
+                    "max_ref": float(np.abs(ref[:, :, sel]).max())})
+    return out
+
+
+def describe(errs: List[Dict[str, float]]) -> str:
+    return "; ".join(f"t{e['chunk']}: max {e['max_abs']:.2e} rms {e['rms']:.1e} |y| {e['max_ref']:.2f}"
+                     for e in errs)

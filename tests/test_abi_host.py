@@ -1,0 +1,149 @@
+"""librehyat C ABI on the host: the library loads, exports every declared entry point, and
+rejects bad arguments with the documented status before anything is launched.
+
+No call here reaches a kernel launch (each one fails validation first), so these run
+without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_softmax_linear_amd as hs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rehyat.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIAS = range(9)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rehyat_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = hs.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    # the binding wraps every declared entry point and nothing else
+    assert set(hs.exported_symbols()) == set(names)
+
+
+def test_status_strings():
+    L = hs.lib()
+    names = [L.rehyat_status_str(i).decode() for i in range(9)]
+    assert names == ["REHYAT_OK", "REHYAT_ERR_NULL", "REHYAT_ERR_SHAPE", "REHYAT_ERR_DTYPE",
+                     "REHYAT_ERR_ALIGN", "REHYAT_ERR_UNSUPPORTED", "REHYAT_ERR_WORKSPACE",
+                     "REHYAT_ERR_HIP", "REHYAT_ERR_ALIAS"]
+
+
+def _desc(**kw):
+    base = dict(B=2, H=3, T=7, HW=10, D=128, F=128, Tc=3, To=1, dtype=hs.BF16, y_dtype=hs.F32,
+                mode=hs.CAUSAL, w_per_head=0)
+    base.update(kw)
+    return hs.Desc(**base)
+
+
+# Fake, well-separated, 16-byte aligned "device addresses": validation never dereferences them.
+P = [0x10000000 * (i + 1) for i in range(16)]
+
+
+def fwd(desc, q=P[0], k=P[1], v=P[2], Wq=P[3], Wk=P[4], y=P[5], ws=P[6], ws_bytes=None):
+    L = hs.lib()
+    if ws_bytes is None:
+        ws_bytes = L.rehyat_hybrid_fwd_workspace(ctypes.byref(desc.c())) if desc else 0
+    d = ctypes.byref(desc.c()) if desc is not None else None
+    return L.rehyat_hybrid_fwd(d, q, k, v, Wq, Wk, y, ws, ws_bytes, None)
+
+
+def step(desc, t=1, q=P[0], k=P[1], v=P[2], Wq=P[3], Wk=P[4], S=P[5], z=P[6], kt=P[7], vt=P[8],
+         y=P[9], ws=P[10], ws_bytes=None):
+    L = hs.lib()
+    if ws_bytes is None:
+        ws_bytes = L.rehyat_recurrent_step_workspace(ctypes.byref(desc.c()))
+    return L.rehyat_recurrent_step(ctypes.byref(desc.c()), t, q, k, v, Wq, Wk, S, z, kt, vt, y,
+                                   ws, ws_bytes, None)
+
+
+def test_hybrid_fwd_validation():
+    d = _desc()
+    assert fwd(None) == ERR_NULL
+    assert "desc" in hs.lib().rehyat_last_error().decode()
+    assert fwd(d, q=None) == ERR_NULL
+    assert fwd(d, y=None) == ERR_NULL
+    assert fwd(_desc(dtype=7)) == ERR_DTYPE
+    assert fwd(_desc(y_dtype=2)) == ERR_DTYPE
+    assert fwd(_desc(mode=3)) == ERR_DTYPE
+    assert fwd(_desc(B=0)) == ERR_SHAPE
+    assert fwd(_desc(To=-1)) == ERR_SHAPE
+    assert fwd(_desc(Tc=0)) == ERR_SHAPE
+    assert fwd(_desc(w_per_head=2)) == ERR_SHAPE
+    assert fwd(_desc(D=64)) == ERR_UNSUP            # bf16 path: D = 128 only
+    assert fwd(_desc(F=96)) == ERR_UNSUP
+    assert fwd(_desc(dtype=hs.F32, D=96)) == ERR_UNSUP
+    assert fwd(_desc(dtype=hs.F32, F=40)) == ERR_UNSUP
+    assert fwd(_desc(B=1 << 12, H=1 << 10)) == ERR_SHAPE   # > 2^31 elements
+    assert fwd(d, q=P[0] + 8) == ERR_ALIGN
+    assert fwd(d, ws=None) == ERR_WS
+    need = hs.lib().rehyat_hybrid_fwd_workspace(ctypes.byref(d.c()))
+    assert fwd(d, ws_bytes=need - 1) == ERR_WS
+    assert fwd(d, y=P[0]) == ERR_ALIAS              # y aliases q
+    assert fwd(d, ws=P[1] + 64) == ERR_ALIAS        # workspace inside k
+
+
+def test_workspace_sizes():
+    L = hs.lib()
+    d = _desc()
+    E = d.F * d.D + d.F
+    BH = d.B * d.H
+    assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == BH * (d.T + d.n_chunks) * E * 4
+    assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == BH * d.Tc * E * 4
+    assert L.rehyat_state_update_workspace(ctypes.byref(d.c()), 1000) == BH * 2 * E * 4
+    assert L.rehyat_state_update_workspace(ctypes.byref(d.c()), 0) == 0
+    assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(_desc(D=64).c())) == 0   # invalid desc
+
+
+def test_recurrent_step_validation():
+    d = _desc()
+    assert step(_desc(To=4)) == ERR_UNSUP                  # To > Tc
+    assert step(d, t=-1) == ERR_SHAPE
+    assert step(d, t=d.n_chunks) == ERR_SHAPE
+    assert step(_desc(T=7, Tc=3, To=2), t=2) == ERR_UNSUP  # last chunk has 1 frame < To
+    assert step(d, kt=None) == ERR_NULL
+    assert step(d, S=None) == ERR_NULL
+    assert step(d, z=P[5] + 4) == ERR_ALIGN
+    assert step(d, ws_bytes=0) == ERR_WS
+    assert step(d, y=P[2]) == ERR_ALIAS                    # y_c aliases v_c
+    assert step(d, S=P[5], z=P[5] + 16) == ERR_ALIAS       # z inside S
+
+
+def test_phi_and_state_update_validation():
+    L = hs.lib()
+    d = _desc()
+    # n = 0 is a no-op that succeeds without touching the device
+    assert L.rehyat_phi(ctypes.byref(d.c()), P[0], 0, P[1], P[2], None) == OK
+    assert L.rehyat_phi(ctypes.byref(d.c()), None, 10, P[1], P[2], None) == ERR_NULL
+    assert L.rehyat_phi(ctypes.byref(d.c()), P[0], -1, P[1], P[2], None) == ERR_SHAPE
+    assert L.rehyat_phi(ctypes.byref(d.c()), P[0], 10, P[1], P[0], None) == ERR_ALIAS
+    assert L.rehyat_phi(ctypes.byref(d.c()), P[0] + 2, 10, P[1], P[2], None) == ERR_ALIGN
+    ws = L.rehyat_state_update_workspace(ctypes.byref(d.c()), 100)
+    assert L.rehyat_state_update(ctypes.byref(d.c()), P[0], P[1], 0, P[2], P[3], P[4], None, 0,
+                                 None) == OK
+    assert L.rehyat_state_update(ctypes.byref(d.c()), P[0], P[1], 100, P[2], P[3], P[4], P[5],
+                                 ws - 4, None) == ERR_WS
+    assert L.rehyat_state_update(ctypes.byref(d.c()), P[0], P[1], 100, P[2], None, P[4], P[5], ws,
+                                 None) == ERR_NULL
+    assert L.rehyat_state_update(ctypes.byref(d.c()), P[0], P[1], 100, P[2], P[0], P[4], P[5], ws,
+                                 None) == ERR_ALIAS
+
+
+def test_python_binding_raises():
+    d = _desc()
+    with pytest.raises(hs.RehyatError) as e:
+        hs.rehyat_hybrid_fwd(d, P[0], P[1], P[2], P[3], P[4], P[5], None, 0, stream=0)
+    assert e.value.name == "REHYAT_ERR_WORKSPACE"
