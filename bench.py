@@ -1,0 +1,255 @@
+"""Throughput of ReHyAt hybrid attention on one MI355X (librehyat, bf16 MFMA).
+
+Workload (the metric's configuration): the 21x30x52 latent of a 5 s 480x832 video,
+batch 2 (cond/uncond), 12 heads, D = F = 128, chunks of Tc = 3 frames with To = 1 overlap
+frame, causal form; bf16 q, k, v, W with fp32 accumulation and fp32 output; synthetic
+seeded inputs with a per-head scale (synthetic/__init__.py).
+
+A step is one call of rehyat_hybrid_fwd (causal): phi(k) and the per-frame state sums,
+the exclusive scan to the per-chunk states, then the attention kernel (phi(q), linear
+read-out, windowed softmax and joint normalisation fused). Inputs are resident in HBM.
+
+Printed JSON line: tokens/s (value), ms per step, TFLOP/s and fraction of the bf16 MFMA
+peak over the whole step, the roofline of the dominant kernel (the attention kernel,
+timed with HIP events recorded by the library on its launch stream), the float64 CPU
+oracle timed on a bounded sample (cpu_baseline), and context timings: the same step as 7
+recurrent steps, the bidirectional form, and full softmax attention of the same shape
+(one chunk covering the whole sequence) with librehyat and with torch's SDPA.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-context]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attn tokens/s & TFLOP/s per MI355X at 21×30×52, % of MFMA peak"
+MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 flop/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+
+
+def flop_model(B, H, T, HW, D, F, Tc, To, causal=True):
+    """Algorithmic FLOPs (only what the method needs: no padding, no masked pairs).
+
+    window pairs: 4*D each (q.k and p*v); phi(q), phi(k): 2*D*F per row each; linear
+    read-out phi(q) S: 2*F*D per query row with a non-empty linear set; state phi(k)^T v:
+    2*F*D per key that enters some linear set.
+    Returns (total, attention-kernel part, state-kernel part, window pairs per head).
+    """
+    N, Np = T * HW, Tc * HW
+    pairs = rows_lin = 0
+    t = 0
+    while t * Np < N:
+        r0, r1 = t * Np, min((t + 1) * Np, N)
+        lo, hi = max(t * Np - To * HW, 0), r1
+        pairs += (r1 - r0) * (hi - lo)
+        if lo > 0 or (not causal and hi < N):
+            rows_lin += r1 - r0
+        t += 1
+    last_lo = max((t - 1) * Np - To * HW, 0)
+    keys_state = N if not causal else last_lo
+    attn = 4 * D * pairs + 2 * D * F * rows_lin + 2 * F * D * rows_lin
+    state = 2 * D * F * keys_state + 2 * F * D * keys_state
+    BH = B * H
+    return BH * (attn + state), BH * attn, BH * state, pairs
+
+
+# ---- CPU baseline: the float64 oracle on a bounded sample --------------------------------
+
+def _oracle_head(args):
+    from threadpoolctl import threadpool_limits
+    import oracle as orc
+    q, k, v, W, HW, Tc, To = args
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        orc.hybrid_attention(q, k, v, W, W, HW=HW, Tc=Tc, To=To, causal=True)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(inp, cfg):
+    """Time the oracle on whole heads of the workload, one head per worker process.
+
+    Runs before the GPU is touched (worker processes are forked). Returns the
+    cpu_baseline JSON object, in tokens/s of the full workload."""
+    import multiprocessing as mp
+    import synthetic as syn
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, 16, cfg.B * cfg.H))
+    W = syn.to_f64(inp["W"])
+    jobs = []
+    for i in range(workers):
+        b, h = divmod(i, cfg.H)
+        jobs.append((syn.to_f64(inp["q"][b, h]), syn.to_f64(inp["k"][b, h]),
+                     syn.to_f64(inp["v"][b, h]), W, cfg.HW, cfg.Tc, cfg.To))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        per_head = pool.map(_oracle_head, jobs)
+    wall = time.perf_counter() - t0
+    heads_total = cfg.B * cfg.H
+    # whole workload = B*N tokens through all B*H heads, at the sampled rate
+    tokens_per_s = cfg.B * cfg.N / (wall * heads_total / workers)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{workers} of {heads_total} heads of the same workload (all {cfg.N} query "
+                      f"rows each), one head per process, 1 BLAS thread each; wall {wall:.1f} s, "
+                      f"mean {sum(per_head) / len(per_head):.1f} s per head; scaled to all heads",
+            "host_cores_visible": cores}
+
+
+# ---- GPU timing -----------------------------------------------------------------------
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}); per-GPU throughput is the value at --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synthetic as syn
+    import hybrid_softmax_linear_amd as hs
+    from hybrid_softmax_linear_amd import torch_api as ta
+
+    hs.lib()   # fail loudly if the HIP library is missing
+    cfg = syn.config(3)
+    inp = syn.make_inputs(cfg)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
+    print(f"# cpu baseline done: {cpu and round(cpu['value'], 1)} tokens/s", file=sys.stderr,
+          flush=True)
+
+    dev = torch.device("cuda:0")
+    q, k, v, W = (inp[n].to(dev) for n in ("q", "k", "v", "W"))
+    desc = hs.Desc(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, F=cfg.F, Tc=cfg.Tc, To=cfg.To,
+                   dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL)
+    ws = ta.workspace(hs.rehyat_hybrid_fwd_workspace(desc), dev)
+    y = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        hs.rehyat_hybrid_fwd(desc, q, k, v, W, W, y, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hs.rehyat_timing_enable(True)
+    ms = time_calls(step, args.steps, 0)
+    kern_ms, launches = hs.rehyat_timing_read()
+    hs.rehyat_timing_enable(False)
+    kern_avg = kern_ms / max(launches, 1)
+
+    total_flop, attn_flop, state_flop, pairs = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D,
+                                                          cfg.F, cfg.Tc, cfg.To, causal=True)
+    tokens = cfg.B * cfg.N
+    tflops = total_flop / (ms * 1e-3) / 1e12
+    attn_tflops = attn_flop / (kern_avg * 1e-3) / 1e12
+    print(f"# step {ms:.3f} ms, attention kernel {kern_avg:.3f} ms ({launches} launches)",
+          file=sys.stderr, flush=True)
+
+    context = {}
+    if not args.no_context:
+        # the same causal computation as 7 recurrent steps (chunks resident, contiguous)
+        Np = cfg.Tc * cfg.HW
+        chunks = [tuple(x[:, :, t * Np:(t + 1) * Np].contiguous() for x in (q, k, v))
+                  for t in range(cfg.n_chunks)]
+        rec = ta.Recurrent(cfg.B, cfg.H, cfg.D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
+                           device=dev)
+        yc = torch.empty(chunks[0][0].shape, dtype=torch.float32, device=dev)
+
+        def rec_pass():
+            rec.t = 0
+            for (qc, kc, vc) in chunks:
+                rec.step(qc, kc, vc, W, out=yc)
+
+        rec_ms = time_calls(rec_pass, max(3, args.steps // 2), 2)
+        context["recurrent_7_steps_ms"] = rec_ms
+        context["recurrent_tokens_per_s"] = tokens / (rec_ms * 1e-3)
+        del chunks, rec, yc
+        # bidirectional chunked form, same shape
+        dbi = hs.Desc(**{**desc.__dict__, "mode": hs.BIDIR})
+        wsb = ta.workspace(hs.rehyat_hybrid_fwd_workspace(dbi), dev)
+        bi_ms = time_calls(lambda: hs.rehyat_hybrid_fwd(dbi, q, k, v, W, W, y, wsb, stream=stream),
+                           max(3, args.steps // 2), 2)
+        bi_flop = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D, cfg.F, cfg.Tc, cfg.To, causal=False)[0]
+        context["bidir_ms"] = bi_ms
+        context["bidir_tflops"] = bi_flop / (bi_ms * 1e-3) / 1e12
+        del wsb
+        # full softmax attention of the same shape: one chunk spanning all 21 frames
+        dfull = hs.Desc(**{**desc.__dict__, "Tc": cfg.T, "To": 0})
+        wsf = ta.workspace(hs.rehyat_hybrid_fwd_workspace(dfull), dev)
+        full_flop = 4 * cfg.D * cfg.N * cfg.N * cfg.B * cfg.H
+        full_ms = time_calls(lambda: hs.rehyat_hybrid_fwd(dfull, q, k, v, W, W, y, wsf,
+                                                           stream=stream), 3, 1)
+        context["full_softmax_ms"] = full_ms
+        context["full_softmax_tflops"] = full_flop / (full_ms * 1e-3) / 1e12
+        context["full_over_hybrid_time"] = full_ms / ms
+        del wsf
+        try:
+            qs, ks_, vs = q, k, v
+            sdpa = lambda: torch.nn.functional.scaled_dot_product_attention(qs, ks_, vs)
+            sd_ms = time_calls(sdpa, 3, 1)
+            context["torch_sdpa_full_softmax_ms"] = sd_ms
+            context["torch_sdpa_full_softmax_tflops"] = full_flop / (sd_ms * 1e-3) / 1e12
+        except Exception as e:  # third-party context only
+            context["torch_sdpa_error"] = str(e)[:200]
+
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "21x30x52 latent (480x832, 5 s): B2 H12 D128 F128, Tc3 To1, "
+                               "causal, one rehyat_hybrid_fwd call per step",
+                   "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)",
+                   "y_dtype": "fp32"},
+        "tflops": tflops,
+        "mfma_peak_frac": tflops / MFMA_PEAK_BF16_TFLOPS,
+        "flop_per_step": total_flop,
+        "roofline": {"bound": "mfma", "kernel": "hybrid_attn_bf16_kernel<128>",
+                     "achieved": attn_tflops, "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS, "traffic": None,
+                     "flop_per_launch": attn_flop, "avg_launch_ms": kern_avg,
+                     "launches_timed": launches},
+        "cpu_baseline": cpu,
+        "context": context,
+    }
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -124,6 +124,10 @@ struct AttnArgs {
   // head strides. For the whole-sequence form A is the sequence itself and nb = 0.
   const void* ka; const void* va; int64_t a_rows;
   const void* kb; const void* vb; int64_t b_rows;
+  // V^T of the window for the bf16 path: head bh, chunk t_local at
+  // vt + bh*vt_bh + t_local*vt_t, rows d of vt_ld elements; window key 0 sits at column
+  // lo of a row when vt_key0_is_lo (V^T of the whole sequence), else at column 0.
+  const void* vt; int64_t vt_bh, vt_t, vt_ld; int vt_key0_is_lo;
   const void* Wq;       // [D, F] or [H, D, F]
   int w_per_head;
   const float* S;       // linear state of (head, chunk): S + bh*s_bh + t*s_t, [F, D]
@@ -154,6 +158,8 @@ struct StateArgs {
   const void* Wk; int w_per_head; int H;
   float* part;          // [BH, n_seg, F*D + F] fp32 partial (S then z)
   float u_scale;
+  // optional (bf16 path): V^T of the virtual rows, [BH][D][vt_ld] bf16, column = row index
+  void* vt_out; int64_t vt_ld;
 };
 
 }  // namespace rehyat
