@@ -34,10 +34,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librehyat)")
 
 
+# Per-file extra flags. The attention kernel keeps its MFMA results in VGPRs (the softmax
+# reads every S^T element with VALU; AGPR results would need a copy per element).
+EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + lang + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + lang + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature flag; that warning is harmless
     noise = "is not a recognized feature for this target"

@@ -1,16 +1,17 @@
 // attn_bf16.hip - hybrid softmax/linear attention forward on bf16 MFMA (gfx950), D = 128.
 //
-// One workgroup (4 waves) computes 256 query rows of one chunk of one head:
+// One workgroup (8 waves, two per SIMD) computes 256 query rows of one chunk of one head:
 //   y = (sum_window exp(q.k/sqrt(D)) v + a^L) / (sum_window exp(q.k/sqrt(D)) + n^L)
 // (joint normalisation of the softmax and linear branches, papernotes.org ReHyAt note,
 // key design 1; window = the chunk plus To earlier frames, key design 2; linear branch
 // a^L = phi(q) S, n^L = phi(q) z from the carried state, key design 4).
 //
-// Each wave owns 64 queries (two 32-query MFMA column blocks). Work is done transposed:
+// Each wave owns 32 queries (one 32-query MFMA column block); the two waves sharing a SIMD
+// hide each other's softmax and LDS latency behind their MFMAs. Work is done transposed:
 // S^T = K Q^T (A = K from LDS, B = Q^T held in registers), so each lane owns one query
 // column and the sums over keys stay inside the lane pair (l, l^32); the exponentiated
 // tile P^T feeds O^T = V^T P^T as the B operand without leaving registers. K tiles
-// ([64 keys][128 d]) and V^T tiles ([128 d][64 keys], from a V^T copy in HBM) stream into
+// ([128 keys][128 d]) and V^T tiles ([128 d][128 keys], from a V^T copy in HBM) stream into
 // LDS by buffer loads that write LDS directly (no staging registers); rows past the window
 // come back as zeros from the buffer descriptor's range check.
 //
@@ -30,22 +31,26 @@ namespace rehyat {
 
 namespace {
 
-constexpr int NW = 4;           // waves per workgroup
-constexpr int QW = 64;          // queries per wave
+constexpr int NW = 8;           // waves per workgroup
+constexpr int QW = 32;          // queries per wave
+constexpr int NT = NW * 64;     // threads per workgroup
 constexpr int QT = NW * QW;     // queries per workgroup
 constexpr float kNegBig = -3.0e38f;
-constexpr int kStageBytes = kKTileBytes + kVTileBytes;   // 32 KB: K tile + V^T tile
+constexpr int kKeys = 128;                               // keys per LDS tile
+constexpr int kKBytes = kKeys * 256;                     // K tile [128 keys][128 d] bf16
+constexpr int kVBytes = kKeys * 256;                     // V^T tile [128 d][128 keys] bf16
+constexpr int kStageBytes = kKBytes + kVBytes;           // 64 KB per stage
 constexpr int kBufRsrcWord3 = 0x00020000;                // gfx9 buffer descriptor word 3
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct QRegs {
-  bf16x8 op[2][8];              // B operand of S^T = K Q^T: [q block][d step]
+  bf16x8 op[8];                 // B operand of S^T = K Q^T: [d step]
 };
 
 struct Acc {
-  f32x16 O[2][4];               // O^T accumulators: [q block][d block]
-  float l[2];                   // partial weight sums of this lane's keys
+  f32x16 O[4];                  // O^T accumulators: [d block]
+  float l;                      // partial weight sum of this lane's keys
 };
 
 // Per-workgroup geometry of one (head, chunk, query tile).
@@ -66,50 +71,50 @@ struct Src {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
-// Issue the direct-to-LDS loads of tile kt into one stage (4 + 4 per thread).
+// V^T tile layout: row d (256 B = 128 keys), 16-byte chunk c (keys 8c..8c+7) stored at
+// chunk c ^ (d & 15), so 16 consecutive d rows read at one logical chunk hit 16 distinct
+// bank groups.
+__device__ __forceinline__ int vt128_off(int d, int c) { return d * 256 + ((c ^ (d & 15)) << 4); }
+
+// Issue the direct-to-LDS loads of tile kt into one stage (4 + 4 per thread). Each
+// instruction writes 1 KB of LDS contiguously (lane i -> bytes 16i..16i+15), so the
+// swizzles are applied by choosing which global chunk each lane fetches.
 __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* stage, int wave,
                                          int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int it = wave * 4 + i;
-    // K: LDS bytes [it*1 KB, +1 KB) hold rows 4it..4it+3; physical chunk lane%16
-    const int r = 4 * it + (lane >> 4);
-    const int c = (lane & 15) ^ kappa(r & 15);
+    const int r = 4 * it + (lane >> 4);         // K row / V^T row of this lane
+    const int pc = lane & 15;                   // physical chunk
+    const int ck = pc ^ kappa(r & 15);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, (lds_void*)(stage + it * 1024), 16,
-                                             (kt * kTileRows + r) * 256 + c * 16, 0, 0, 0);
-    // V^T: LDS bytes [16 KB + it*1 KB, +1 KB) hold d rows 8it..8it+7; physical chunk lane%8
-    const int d = 8 * it + (lane >> 3);
-    const int kc = (lane & 7) ^ ((d + (d >> 3)) & 7);
+                                             (kt * kKeys + r) * 256 + ck * 16, 0, 0, 0);
+    const int cv = pc ^ (r & 15);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        s.vt, (lds_void*)(stage + kKTileBytes + it * 1024), 16,
-        d * s.vt_ld_bytes + s.vt_key0_bytes + (kt * kTileRows + 8 * kc) * 2, 0, 0, 0);
+        s.vt, (lds_void*)(stage + kKBytes + it * 1024), 16,
+        r * s.vt_ld_bytes + s.vt_key0_bytes + (kt * kKeys + 8 * cv) * 2, 0, 0, 0);
   }
 }
 
-// S^T block (32 keys x 64 queries) of one 32-key block of the K tile in LDS.
-__device__ __forceinline__ void qk_block(f32x16 (&Sc)[2], const unsigned char* kbuf, int kb,
-                                         const QRegs& Q, int lane) {
+// S^T block (32 keys x 32 queries) of 32-key block kb of the K tile in LDS.
+__device__ __forceinline__ f32x16 qk_block(const unsigned char* kbuf, int kb, const QRegs& Q,
+                                           int lane) {
+  f32x16 S;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Sc[qb][i] = 0.0f;
+  for (int i = 0; i < 16; ++i) S[i] = 0.0f;
   const int arow = 32 * kb + kappa(lane & 31);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     bf16x8 av = as_bf16x8(lds_read16(kbuf, ktile_off(arow, 2 * s + (lane >> 5))));
-    Sc[0] = mfma32(av, Q.op[0][s], Sc[0]);
-    Sc[1] = mfma32(av, Q.op[1][s], Sc[1]);
+    S = mfma32(av, Q.op[s], S);
   }
+  return S;
 }
 
-__device__ __forceinline__ void mask_block(f32x16 (&Sc)[2], int key0, int nk, int lane) {
+__device__ __forceinline__ void mask_block(f32x16& S, int key0, int nk, int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (key0 + cidx(i, lane) >= nk) {
-      Sc[0][i] = -__builtin_inff();
-      Sc[1][i] = -__builtin_inff();
-    }
-  }
+  for (int i = 0; i < 16; ++i)
+    if (key0 + cidx(i, lane) >= nk) S[i] = -__builtin_inff();
 }
 
 __device__ __forceinline__ float rowmax16(const f32x16& v) {
@@ -120,56 +125,50 @@ __device__ __forceinline__ float rowmax16(const f32x16& v) {
 }
 
 // p = 2^(s*ls - m0) as bf16 (the B operand of O^T += V^T P^T); l += sum of the rounded p.
-__device__ __forceinline__ void softmax_block(bf16x8 (&P)[2][2], float (&l)[2],
-                                              const f32x16 (&Sc)[2], const float (&m0)[2],
-                                              float ls) {
+__device__ __forceinline__ void softmax_block(bf16x8 (&P)[2], float& l, const f32x16& S,
+                                              float m0, float ls) {
   const bf16x2 ones{(bf16)1.0f, (bf16)1.0f};
+  float acc = 0.0f;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float acc = 0.0f;
+  for (int j = 0; j < 2; ++j) {
+    u32x4 pk;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i0 = 8 * j + 2 * e;
-        bf16x2 pb = pack_bf16(fast_exp2(Sc[qb][i0] * ls - m0[qb]),
-                              fast_exp2(Sc[qb][i0 + 1] * ls - m0[qb]));
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
-        pk[e] = __builtin_bit_cast(unsigned, pb);
-      }
-      P[qb][j] = as_bf16x8(pk);
+    for (int e = 0; e < 4; ++e) {
+      const int i0 = 8 * j + 2 * e;
+      bf16x2 pb = pack_bf16(fast_exp2(S[i0] * ls - m0), fast_exp2(S[i0 + 1] * ls - m0));
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
+      pk[e] = __builtin_bit_cast(unsigned, pb);
     }
-    l[qb] += acc;
+    P[j] = as_bf16x8(pk);
   }
+  l += acc;
 }
 
-__device__ __forceinline__ void pv_block(Acc& A, const bf16x8 (&P)[2][2], const unsigned char* vbuf,
+__device__ __forceinline__ void pv_block(Acc& A, const bf16x8 (&P)[2], const unsigned char* vbuf,
                                          int kb, int lane) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int d = 32 * db + (lane & 31);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      bf16x8 av = as_bf16x8(lds_read16(vbuf, vtile_chunk_off(d, 4 * kb + 2 * j + (lane >> 5))));
-      A.O[0][db] = mfma32(av, P[0][j], A.O[0][db]);
-      A.O[1][db] = mfma32(av, P[1][j], A.O[1][db]);
+      bf16x8 av = as_bf16x8(lds_read16(vbuf, vt128_off(d, 4 * kb + 2 * j + (lane >> 5))));
+      A.O[db] = mfma32(av, P[j], A.O[db]);
     }
   }
 }
 
-// Linear branch: O = a^L^T = S^T phi(Q)^T (bf16 MFMA) and n^L = phi(q).z per q block
-// (full sum over the lane pair). Uses smem as W^T / S^T staging; ends with a barrier.
+// Linear branch: O = a^L^T = S^T phi(Q)^T (bf16 MFMA) and n^L = phi(q).z (full sum over
+// the lane pair). Uses smem as W^T / S^T staging; ends with a barrier.
 template <int F>
-__device__ __forceinline__ void linear_branch(Acc& A, float (&nlf)[2], const AttnArgs& a,
+__device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs& a,
                                               const Geo& g, const QRegs& Q, unsigned char* smem,
                                               float* zs, int tid, int lane) {
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.Wq) +
                       (a.w_per_head ? (int64_t)g.h * kDim * F : 0);
   const float* S = a.S + g.bh * a.s_bh + g.t_local * a.s_t;
   const float* z = a.z + g.bh * a.z_bh + g.t_local * a.z_t;
-  float nl[2] = {0.0f, 0.0f};
-  for (int f = tid; f < F; f += 256) zs[f] = z[f];
+  float nl = 0.0f;
+  for (int f = tid; f < F; f += NT) zs[f] = z[f];
   constexpr int FS = F < 128 ? F : 128;   // features per LDS slab
   constexpr int NCH = FS / 8;             // 16-byte chunks per S^T row
   unsigned char* wt = smem;               // [FS][128] bf16, K-tile layout
@@ -177,9 +176,9 @@ __device__ __forceinline__ void linear_branch(Acc& A, float (&nlf)[2], const Att
 #pragma unroll 1
   for (int f0 = 0; f0 < F; f0 += FS) {
     if (f0 > 0) __syncthreads();
-    stage_wt(wt, W, F, f0, FS, tid);
+    if (tid < 256) stage_wt(wt, W, F, f0, FS, tid);   // stage_wt is written for 256 threads
     // S^T slab: thread reads S[f][4*d4 .. +4] (fp32) and scatters 4 bf16 into column f.
-    for (int id = tid; id < FS * 32; id += 256) {
+    for (int id = tid; id < FS * 32; id += NT) {
       const int fl = id % FS, d4 = id / FS;
       f32x4 v = *reinterpret_cast<const f32x4*>(S + (int64_t)(f0 + fl) * kDim + 4 * d4);
 #pragma unroll
@@ -193,38 +192,32 @@ __device__ __forceinline__ void linear_branch(Acc& A, float (&nlf)[2], const Att
 #pragma unroll 1
     for (int fb = 0; fb < FS / 32; ++fb) {
       // U^T block: rows = features 32fb + kappa(l%32) (A = W^T), cols = queries (B = Q^T)
-      f32x16 U[2];
+      f32x16 U;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) U[qb][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) U[i] = 0.0f;
       const int arow = 32 * fb + kappa(lane & 31);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         bf16x8 av = as_bf16x8(lds_read16(wt, ktile_off(arow, 2 * s + (lane >> 5))));
-        U[0] = mfma32(av, Q.op[0][s], U[0]);
-        U[1] = mfma32(av, Q.op[1][s], U[1]);
+        U = mfma32(av, Q.op[s], U);
       }
       // phi = 1 + u + u^2/2, rounded to bf16: B operand of a^L^T = S^T phi^T.
-      bf16x8 P[2][2];
+      bf16x8 P[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int j = 0; j < 2; ++j) {
+        u32x4 pk;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i0 = 8 * j + 2 * e;
-            float u0 = U[qb][i0] * a.u_scale, u1 = U[qb][i0 + 1] * a.u_scale;
-            float p0 = 1.0f + u0 + 0.5f * u0 * u0;
-            float p1 = 1.0f + u1 + 0.5f * u1 * u1;
-            unsigned w = pack_bf16_u32(p0, p1);
-            pk[e] = w;
-            const int f = f0 + 32 * fb + cidx(i0, lane);
-            nl[qb] += bf16_lo(w) * zs[f] + bf16_hi(w) * zs[f + 1];
-          }
-          P[qb][j] = as_bf16x8(pk);
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = 8 * j + 2 * e;
+          float u0 = U[i0] * a.u_scale, u1 = U[i0 + 1] * a.u_scale;
+          float p0 = 1.0f + u0 + 0.5f * u0 * u0;
+          float p1 = 1.0f + u1 + 0.5f * u1 * u1;
+          unsigned w = pack_bf16_u32(p0, p1);
+          pk[e] = w;
+          const int f = f0 + 32 * fb + cidx(i0, lane);
+          nl += bf16_lo(w) * zs[f] + bf16_hi(w) * zs[f + 1];
         }
+        P[j] = as_bf16x8(pk);
       }
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -233,80 +226,59 @@ __device__ __forceinline__ void linear_branch(Acc& A, float (&nlf)[2], const Att
         for (int j = 0; j < 2; ++j) {
           const int c = 4 * fb + 2 * j + (lane >> 5);
           bf16x8 av = as_bf16x8(lds_read16(st, d * (FS * 2) + ((c ^ (d & (NCH - 1))) << 4)));
-          A.O[0][db] = mfma32(av, P[0][j], A.O[0][db]);
-          A.O[1][db] = mfma32(av, P[1][j], A.O[1][db]);
+          A.O[db] = mfma32(av, P[j], A.O[db]);
         }
       }
     }
   }
-  nlf[0] = pair_sum(nl[0]);
-  nlf[1] = pair_sum(nl[1]);
+  nlf = pair_sum(nl);
   __syncthreads();
 }
 
 __device__ __forceinline__ void zero_acc(Acc& A) {
+  A.l = 0.0f;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    A.l[qb] = 0.0f;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) A.O[qb][db][i] = 0.0f;
-  }
+    for (int i = 0; i < 16; ++i) A.O[db][i] = 0.0f;
 }
 
 // With O = a^L (from linear_branch) and reference m0: O = a^L/n^L * w, l = w (in one lane
 // of the pair), w = 2^(log2 n^L - m0), the weight of the linear "key".
-__device__ __forceinline__ void scale_linear(Acc& A, const float (&nl)[2], const float (&m0)[2],
-                                             int lane) {
+__device__ __forceinline__ void scale_linear(Acc& A, float nl, float m0, int lane) {
+  const float w = fast_exp2(fast_log2(nl) - m0);
+  const float sc = w / nl;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float w = fast_exp2(fast_log2(nl[qb]) - m0[qb]);
-    const float sc = w / nl[qb];
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) A.O[qb][db][i] *= sc;
-    A.l[qb] = (lane < 32) ? w : 0.0f;
-  }
+    for (int i = 0; i < 16; ++i) A.O[db][i] *= sc;
+  A.l = (lane < 32) ? w : 0.0f;
 }
 
-// One 64-key tile from LDS: per 32-key block, S^T = K Q^T, p = 2^(s*ls - m0), l += sum p,
-// O^T += V^T P^T. The last tile of the window masks keys >= nk.
+// One 128-key tile from LDS: four 32-key blocks of S^T = K Q^T, p = 2^(s*ls - m0),
+// l += sum p, O^T += V^T P^T. The last tile of the window masks keys >= nk.
 template <bool kLastTile>
-__device__ __forceinline__ void process_tile(Acc& A, const float (&m0)[2],
-                                             const unsigned char* stage, int kt, int nk,
-                                             const QRegs& Q, float ls, int lane) {
+__device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned char* stage, int kt,
+                                             int nk, const QRegs& Q, float ls, int lane) {
   const unsigned char* kbuf = stage;
-  const unsigned char* vbuf = stage + kKTileBytes;
+  const unsigned char* vbuf = stage + kKBytes;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key0 = kt * kTileRows + kb * 32;
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key0 = kt * kKeys + kb * 32;
     if (kLastTile && key0 >= nk) break;
-    f32x16 Sc[2];
-    qk_block(Sc, kbuf, kb, Q, lane);
-    if (kLastTile) mask_block(Sc, key0, nk, lane);
-    bf16x8 P[2][2];
-    softmax_block(P, A.l, Sc, m0, ls);
+    f32x16 S = qk_block(kbuf, kb, Q, lane);
+    if (kLastTile) mask_block(S, key0, nk, lane);
+    bf16x8 P[2];
+    softmax_block(P, A.l, S, m0, ls);
     pv_block(A, P, vbuf, kb, lane);
   }
 }
 
-// Row maxima (log2 units) over the 32 keys of block 0 of the tile in stage 0.
-__device__ __forceinline__ void peek_block0(float (&mb)[2], const unsigned char* stage, int nk,
-                                            const QRegs& Q, float ls, int lane) {
-  f32x16 Sc[2];
-  qk_block(Sc, stage, 0, Q, lane);
-  if (nk < 32) mask_block(Sc, 0, nk, lane);
-  mb[0] = pair_max(rowmax16(Sc[0])) * ls;
-  mb[1] = pair_max(rowmax16(Sc[1])) * ls;
-}
-
-// Exact row maxima over the window (log2 units), for the overflow fallback.
-__device__ __forceinline__ void max_sweep(float (&mx)[2], const Src& src, const QRegs& Q,
-                                          unsigned char* smem, float ls, int wave, int lane) {
-  const int ntiles = (src.nk + kTileRows - 1) / kTileRows;
-  mx[0] = mx[1] = kNegBig;
+// Exact row maximum over the window (log2 units), for the overflow fallback.
+__device__ __forceinline__ float max_sweep(const Src& src, const QRegs& Q, unsigned char* smem,
+                                           float ls, int wave, int lane) {
+  const int ntiles = (src.nk + kKeys - 1) / kKeys;
+  float mx = kNegBig;
 #pragma unroll 1
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();
@@ -314,27 +286,23 @@ __device__ __forceinline__ void max_sweep(float (&mx)[2], const Src& src, const 
     wait_vmem();
     __syncthreads();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kt * kTileRows + kb * 32 >= src.nk) break;
-      f32x16 Sc[2];
-      qk_block(Sc, smem, kb, Q, lane);
-      mask_block(Sc, kt * kTileRows + kb * 32, src.nk, lane);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) mx[qb] = fmaxf(mx[qb], rowmax16(Sc[qb]) * ls);
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x16 S = qk_block(smem, kb, Q, lane);
+      mask_block(S, kt * kKeys + kb * 32, src.nk, lane);
+      mx = fmaxf(mx, rowmax16(S) * ls);
     }
   }
-  mx[0] = pair_max(mx[0]);
-  mx[1] = pair_max(mx[1]);
+  mx = pair_max(mx);
   __syncthreads();
+  return mx;
 }
 
 // The key loop over a window whose tile 0 is already in stage 0: double-buffered
 // direct-to-LDS tiles, the last tile peeled (masking).
-__device__ __forceinline__ void key_loop(Acc& A, const float (&m0)[2], const Src& src,
-                                         const QRegs& Q, unsigned char* smem, float ls, int wave,
-                                         int lane) {
+__device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const QRegs& Q,
+                                         unsigned char* smem, float ls, int wave, int lane) {
   const int nk = src.nk;
-  const int ntiles = (nk + kTileRows - 1) / kTileRows;
+  const int ntiles = (nk + kKeys - 1) / kKeys;
 #pragma unroll 1
   for (int kt = 0; kt < ntiles - 1; ++kt) {
     unsigned char* cur = smem + (kt & 1) * kStageBytes;
@@ -349,31 +317,29 @@ __device__ __forceinline__ void key_loop(Acc& A, const float (&m0)[2], const Src
   __syncthreads();
 }
 
-// Load window tile 0 into stage 0 and fix the reference: m0 = max(mlow, block-0 maxima).
-__device__ __forceinline__ void start_window(float (&m0)[2], const float (&mlow)[2],
-                                             const Src& src, const QRegs& Q, unsigned char* smem,
-                                             float ls, int wave, int lane) {
+// Load window tile 0 into stage 0 and fix the reference: max(mlow, block-0 row maximum).
+__device__ __forceinline__ float start_window(float mlow, const Src& src, const QRegs& Q,
+                                              unsigned char* smem, float ls, int wave, int lane) {
   tile_dma(src, 0, smem, wave, lane);
   wait_vmem();
   __syncthreads();
-  float mb[2];
-  peek_block0(mb, smem, src.nk, Q, ls, lane);
-  m0[0] = fmaxf(mlow[0], mb[0]);
-  m0[1] = fmaxf(mlow[1], mb[1]);
+  f32x16 S = qk_block(smem, 0, Q, lane);
+  if (src.nk < 32) mask_block(S, 0, src.nk, lane);
+  return fmaxf(mlow, pair_max(rowmax16(S)) * ls);
 }
 
 template <int F>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 hybrid_attn_bf16_kernel(AttnArgs a) {
-  // 64 KB: two K/V^T stages during the key loop; W^T and S^T slabs for the linear branch.
+  // 128 KB: two K/V^T stages during the key loop; W^T and S^T slabs for the linear branch.
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
   __shared__ float zs[F];
   __shared__ int bad_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int tile = xcd_remap(blockIdx.x, a.nblocks);
 
   Geo g;
@@ -396,16 +362,15 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 
   // ---- Q^T operand registers ----------------------------------------------------------
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + head_off(g.bh, a.q_rows, kDim);
+  const int qrow = g.q_wave0 + (lane & 31);
   QRegs Q;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = g.q_wave0 + qb * 32 + (lane & 31);
+  {
     const bool ok = qrow < g.rows;
     const uint16_t* src = qh + (g.q_row_base + (ok ? qrow : 0)) * kDim + 8 * (lane >> 5);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 v = ok ? *reinterpret_cast<const u32x4*>(src + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      Q.op[qb][s] = as_bf16x8(v);
+      Q.op[s] = as_bf16x8(v);
     }
   }
 
@@ -426,58 +391,50 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   }
   const float ls = a.logit_scale;
 
-  // ---- linear branch, then the key loop ------------------------------------------------
+  // ---- linear branch, reference m0, key loop ------------------------------------------
   Acc A;
-  float m0[2] = {kNegBig, kNegBig}, nl[2] = {1.0f, 1.0f}, ml[2] = {kNegBig, kNegBig};
+  float nl = 1.0f, ml = kNegBig;
   zero_acc(A);
   if (g.has_linear) {
     linear_branch<F>(A, nl, a, g, Q, smem, zs, tid, lane);
-    ml[0] = fast_log2(nl[0]);
-    ml[1] = fast_log2(nl[1]);
+    ml = fast_log2(nl);
   }
-  start_window(m0, ml, src, Q, smem, ls, wave, lane);
+  float m0 = start_window(ml, src, Q, smem, ls, wave, lane);
   if (g.has_linear) scale_linear(A, nl, m0, lane);
   key_loop(A, m0, src, Q, smem, ls, wave, lane);
 
   // ---- overflow guard: recompute the workgroup with the exact row maxima ---------------
   {
-    bool bad = !__builtin_isfinite(A.l[0]) || !__builtin_isfinite(A.l[1]);
+    bool bad = !__builtin_isfinite(A.l);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(A.O[qb][db][i]);
+      for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(A.O[db][i]);
     if (wave_any(bad) && lane == 0) atomicOr(&bad_flag, 1);
     __syncthreads();
     if (bad_flag) {
-      float mx[2];
-      max_sweep(mx, src, Q, smem, ls, wave, lane);
+      const float mx = max_sweep(src, Q, smem, ls, wave, lane);
       zero_acc(A);
       if (g.has_linear) linear_branch<F>(A, nl, a, g, Q, smem, zs, tid, lane);
       // reference = the exact maximum over the linear weight and every window key: every
       // p <= 1 and l >= 1
-      const float mref[2] = {fmaxf(ml[0], mx[0]), fmaxf(ml[1], mx[1])};
-      start_window(m0, mref, src, Q, smem, ls, wave, lane);
+      m0 = start_window(fmaxf(ml, mx), src, Q, smem, ls, wave, lane);
       if (g.has_linear) scale_linear(A, nl, m0, lane);
       key_loop(A, m0, src, Q, smem, ls, wave, lane);
     }
   }
 
   // ---- epilogue: y = O / l ------------------------------------------------------------
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = g.q_wave0 + qb * 32 + (lane & 31);
-    const float inv = 1.0f / pair_sum(A.l[qb]);
-    if (qrow >= g.rows) continue;
+  const float inv = 1.0f / pair_sum(A.l);
+  if (qrow < g.rows) {
     const int64_t off = head_off(g.bh, a.q_rows, kDim) + (g.q_row_base + qrow) * kDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const int d = 32 * db + 8 * gi + 4 * (lane >> 5);
-        float v0 = A.O[qb][db][4 * gi + 0] * inv, v1 = A.O[qb][db][4 * gi + 1] * inv;
-        float v2 = A.O[qb][db][4 * gi + 2] * inv, v3 = A.O[qb][db][4 * gi + 3] * inv;
+        float v0 = A.O[db][4 * gi + 0] * inv, v1 = A.O[db][4 * gi + 1] * inv;
+        float v2 = A.O[db][4 * gi + 2] * inv, v3 = A.O[db][4 * gi + 3] * inv;
         if (a.y_f32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + off + d) = f32x4{v0, v1, v2, v3};
         } else {
@@ -496,7 +453,7 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 int attn_bf16_tile_rows() { return QT; }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int F, hipStream_t stream) {
-  dim3 grid(a.nblocks), block(256);
+  dim3 grid(a.nblocks), block(NT);
   switch (F) {
     case 64:  hipLaunchKernelGGL(hybrid_attn_bf16_kernel<64>, grid, block, 0, stream, a); break;
     case 128: hipLaunchKernelGGL(hybrid_attn_bf16_kernel<128>, grid, block, 0, stream, a); break;
