@@ -103,11 +103,14 @@ __device__ __forceinline__ f32x16 qk_block(const unsigned char* kbuf, int kb, co
 #pragma unroll
   for (int i = 0; i < 16; ++i) S[i] = 0.0f;
   const int arow = 32 * kb + kappa(lane & 31);
+  bf16x8 av[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    bf16x8 av = as_bf16x8(lds_read16(kbuf, ktile_off(arow, 2 * s + (lane >> 5))));
-    S = mfma32(av, Q.op[s], S);
-  }
+  for (int s = 0; s < 8; ++s) av[s] = as_bf16x8(lds_read16(kbuf, ktile_off(arow, 2 * s + (lane >> 5))));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) S = mfma32(av[s], Q.op[s], S);
+  // all eight K fragments in flight before the first MFMA waits on one
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   return S;
 }
 
@@ -146,15 +149,18 @@ __device__ __forceinline__ void softmax_block(bf16x8 (&P)[2], float& l, const f3
 
 __device__ __forceinline__ void pv_block(Acc& A, const bf16x8 (&P)[2], const unsigned char* vbuf,
                                          int kb, int lane) {
+  bf16x8 av[4][2];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + (lane & 31);
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8 av = as_bf16x8(lds_read16(vbuf, vt128_off(d, 4 * kb + 2 * j + (lane >> 5))));
-      A.O[db] = mfma32(av, P[j], A.O[db]);
-    }
-  }
+    for (int j = 0; j < 2; ++j)
+      av[db][j] = as_bf16x8(lds_read16(vbuf, vt128_off(32 * db + (lane & 31), 4 * kb + 2 * j + (lane >> 5))));
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A.O[db] = mfma32(av[db][j], P[j], A.O[db]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 // Linear branch: O = a^L^T = S^T phi(Q)^T (bf16 MFMA) and n^L = phi(q).z (full sum over
@@ -299,8 +305,11 @@ __device__ __forceinline__ float max_sweep(const Src& src, const QRegs& Q, unsig
 
 // The key loop over a window whose tile 0 is already in stage 0: double-buffered
 // direct-to-LDS tiles, the last tile peeled (masking).
+// Waves whose 32 query rows all lie past the chunk (ragged last query tile) only help
+// with the tile loads and barriers.
 __device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const QRegs& Q,
-                                         unsigned char* smem, float ls, int wave, int lane) {
+                                         unsigned char* smem, float ls, int wave, int lane,
+                                         bool active) {
   const int nk = src.nk;
   const int ntiles = (nk + kKeys - 1) / kKeys;
 #pragma unroll 1
@@ -308,12 +317,12 @@ __device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const
     unsigned char* cur = smem + (kt & 1) * kStageBytes;
     unsigned char* nxt = smem + ((kt & 1) ^ 1) * kStageBytes;
     tile_dma(src, kt + 1, nxt, wave, lane);
-    process_tile<false>(A, m0, cur, kt, nk, Q, ls, lane);
+    if (active) process_tile<false>(A, m0, cur, kt, nk, Q, ls, lane);
     wait_vmem();
     __syncthreads();
   }
   const int kt = ntiles - 1;
-  process_tile<true>(A, m0, smem + (kt & 1) * kStageBytes, kt, nk, Q, ls, lane);
+  if (active) process_tile<true>(A, m0, smem + (kt & 1) * kStageBytes, kt, nk, Q, ls, lane);
   __syncthreads();
 }
 
@@ -401,7 +410,8 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   }
   float m0 = start_window(ml, src, Q, smem, ls, wave, lane);
   if (g.has_linear) scale_linear(A, nl, m0, lane);
-  key_loop(A, m0, src, Q, smem, ls, wave, lane);
+  const bool active = g.q_wave0 < g.rows;   // wave-uniform
+  key_loop(A, m0, src, Q, smem, ls, wave, lane, active);
 
   // ---- overflow guard: recompute the workgroup with the exact row maxima ---------------
   {
@@ -420,7 +430,7 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
       // p <= 1 and l >= 1
       m0 = start_window(fmaxf(ml, mx), src, Q, smem, ls, wave, lane);
       if (g.has_linear) scale_linear(A, nl, m0, lane);
-      key_loop(A, m0, src, Q, smem, ls, wave, lane);
+      key_loop(A, m0, src, Q, smem, ls, wave, lane, active);
     }
   }
 

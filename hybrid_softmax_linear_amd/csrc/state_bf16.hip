@@ -69,12 +69,14 @@ state_partial_bf16_kernel(StateArgs a) {
   }
 
   const int ntiles = (nrows + kTileRows - 1) / kTileRows;
+  TileRegs r;
+  tile_load(r, ks, vs, 0, tid);
 #pragma unroll 1
   for (int ti = 0; ti < ntiles; ++ti) {
-    TileRegs r;
-    tile_load(r, ks, vs, (int64_t)ti * kTileRows, tid);
     __syncthreads();   // previous tile fully consumed (and W^T staged on the first pass)
     tile_store(r, kt, vt, tid);
+    // the next tile's global loads fly while this tile is reduced
+    if (ti + 1 < ntiles) tile_load(r, ks, vs, (int64_t)(ti + 1) * kTileRows, tid);
     __syncthreads();
     if (a.vt_out) {
       // V^T of these rows (needs seg_len and the row count multiples of 8): 128 d rows x
