@@ -78,12 +78,13 @@ def phi(x: np.ndarray, W: np.ndarray) -> np.ndarray:
     return 1.0 + u + 0.5 * u * u
 
 
-def _linear_keys(lo: int, hi: int, N: int, causal: bool) -> np.ndarray:
-    """Key indices of the linear set: [0, lo) (causal, key design 4) or its union with
-    [hi, N) (bidirectional: complement of the overlapped window, key design 1)."""
-    if causal:
-        return np.arange(0, lo)
-    return np.concatenate([np.arange(0, lo), np.arange(hi, N)])
+def _linear_ranges(lo: int, hi: int, N: int, causal: bool) -> List[Tuple[int, int]]:
+    """Key ranges of the linear set: [0, lo) (causal, key design 4), plus [hi, N) in the
+    bidirectional form (complement of the overlapped window, key design 1)."""
+    ranges = [(0, lo)] if lo > 0 else []
+    if not causal and hi < N:
+        ranges.append((hi, N))
+    return ranges
 
 
 def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool = True,
@@ -117,21 +118,21 @@ def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool
         sel = np.nonzero((rows_arr >= row_lo) & (rows_arr < row_hi))[0]
         if sel.size == 0:
             continue
-        Lidx = _linear_keys(lo, hi, N, causal)
+        Lr = _linear_ranges(lo, hi, N, causal)
         kS, vS = k[lo:hi], v[lo:hi]
-        phikL, vL = phik[Lidx], v[Lidx]
         for b0 in range(0, sel.size, block):
             pos = sel[b0:b0 + block]
             Qb = q[rows_arr[pos]]
             ES = np.exp((Qb @ kS.T) * inv_sqrt_d)          # softmax branch weights, c_t = 0
             num = ES @ vS
             nS = ES.sum(axis=1)
-            if Lidx.size:
-                EL = phi(Qb, Wq) @ phikL.T                  # linear branch weights
-                num = num + EL @ vL
-                nL = EL.sum(axis=1)
-            else:
-                nL = np.zeros(pos.size)
+            nL = np.zeros(pos.size)
+            if Lr:
+                pq = phi(Qb, Wq)
+                for (a, b) in Lr:
+                    EL = pq @ phik[a:b].T                   # linear branch weights
+                    num = num + EL @ v[a:b]
+                    nL = nL + EL.sum(axis=1)
             y[pos] = num / (nS + nL)[:, None]
             nS_out[pos] = nS
             nL_out[pos] = nL

@@ -29,8 +29,10 @@ F32_BAR = 1e-4
 BF16_BAR = 3e-2
 
 
-def bf16_internal_bar(v: np.ndarray, y_ref: np.ndarray, y_bf16: bool) -> float:
-    bar = 2.0 * 2.0 ** -8 * float(np.abs(v).max())
+def bf16_internal_bar(v, y_ref: np.ndarray, y_bf16: bool) -> float:
+    """v: the values (array or tensor) or their max-abs as a float."""
+    vmax = float(v) if np.isscalar(v) else float(np.abs(np.asarray(v)).max())
+    bar = 2.0 * 2.0 ** -8 * vmax
     if y_bf16:
         bar += 2.0 ** -9 * float(np.abs(y_ref).max())
     return bar
@@ -39,12 +41,21 @@ def bf16_internal_bar(v: np.ndarray, y_ref: np.ndarray, y_bf16: bool) -> float:
 def oracle_rows(inp: Dict[str, torch.Tensor], *, HW: int, Tc: int, To: int, causal: bool,
                 rows: Optional[Sequence[int]] = None,
                 heads: Optional[Iterable] = None) -> np.ndarray:
-    """Oracle output [B, H, len(rows) or N, D] (float64) on the stored inputs."""
-    q, k, v = to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"])
+    """Oracle output [B, H, len(rows) or N, D] (float64) on the stored inputs; heads not
+    listed stay NaN. Inputs are widened to float64 one head at a time."""
+    B, H, N, _ = inp["q"].shape
     Wq = to_f64(inp["W"])
     Wk = to_f64(inp["Wk"]) if "Wk" in inp else Wq
-    return orc.hybrid_attention_bh(q, k, v, Wq, Wk, HW=HW, Tc=Tc, To=To, causal=causal,
-                                   rows=rows, heads=heads)
+    nrows = N if rows is None else len(rows)
+    y = np.full((B, H, nrows, inp["v"].shape[-1]), np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    for (b, h) in pairs:
+        wq = Wq if Wq.ndim == 2 else Wq[h]
+        wk = Wk if Wk.ndim == 2 else Wk[h]
+        y[b, h] = orc.hybrid_attention(to_f64(inp["q"][b, h]), to_f64(inp["k"][b, h]),
+                                       to_f64(inp["v"][b, h]), wq, wk, HW=HW, Tc=Tc, To=To,
+                                       causal=causal, rows=rows)
+    return y
 
 
 def sample_rows(T: int, HW: int, Tc: int, per_edge: int, n_random: int, seed: int = 0) -> List[int]:

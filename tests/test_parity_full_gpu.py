@@ -1,0 +1,111 @@
+"""GPU parity at the full workload sizes (the 320x480 bidirectional, 21x30x52, 81-frame
+streaming and wide-chunk configurations), in the launch configuration bench.py times
+(bf16 inputs, fp32 output, one rehyat_hybrid_fwd call).
+
+The whole output is computed on the GPU; the float64 oracle evaluates a sample of query
+rows one by one (the first and last rows of every chunk plus random rows) for every head.
+The streaming form is checked for bitwise equality with the whole-sequence form at full
+size, and for flat device memory across its 27 steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_softmax_linear_amd as hs
+from hybrid_softmax_linear_amd import torch_api as ta
+import synthetic as syn
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check_rows(y_rows, ref, inp, cfg, rows, label):
+    errs = pu.chunk_errors(y_rows, ref, rows, cfg.T, cfg.HW, cfg.Tc)
+    err = max(e["max_abs"] for e in errs)
+    bar = pu.bf16_internal_bar(inp["v"].abs().max().float().item(), ref, False)
+    print(f"[{label}] max-abs {err:.3e} (bars {pu.BF16_BAR:.0e}, internal {bar:.2e}); "
+          f"{pu.describe(errs)}", flush=True)
+    assert np.isfinite(y_rows).all()
+    assert err <= pu.BF16_BAR
+    assert err <= bar
+
+
+def _fwd(cfg, inp):
+    d = {k: v.to(DEV) for k, v in inp.items() if k in ("q", "k", "v", "W")}
+    y = ta.hybrid_fwd(d["q"], d["k"], d["v"], d["W"], HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
+                      causal=cfg.mode == "causal", y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return d, y
+
+
+@pytest.mark.parametrize("i", [2, 3, 5])
+def test_full_workload_whole_sequence(i):
+    cfg = syn.config(i)
+    inp = syn.make_inputs(cfg)
+    _, y = _fwd(cfg, inp)
+    rows = pu.sample_rows(cfg.T, cfg.HW, cfg.Tc, per_edge=16, n_random=48, seed=i)
+    y_rows = y[:, :, rows].double().cpu().numpy()
+    ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=cfg.mode == "causal",
+                         rows=rows)
+    _check_rows(y_rows, ref, inp, cfg, rows, cfg.name)
+
+
+@pytest.mark.parametrize("i", [3, 5])
+def test_full_workload_recurrent_equals_whole(i):
+    """The causal workloads run as the chunk-wise RNN (one call per chunk) give exactly the
+    whole-sequence result."""
+    cfg = syn.config(i)
+    inp = syn.make_inputs(cfg)
+    d, y = _fwd(cfg, inp)
+    rec = ta.Recurrent(cfg.B, cfg.H, cfg.D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
+                       device=DEV)
+    Np = cfg.Tc * cfg.HW
+    for t in range(cfg.n_chunks):
+        r0, r1 = t * Np, min((t + 1) * Np, cfg.N)
+        yc = rec.step(d["q"][:, :, r0:r1].contiguous(), d["k"][:, :, r0:r1].contiguous(),
+                      d["v"][:, :, r0:r1].contiguous(), d["W"])
+        assert torch.equal(yc, y[:, :, r0:r1]), f"chunk {t} differs"
+
+
+def test_streaming_81_frames_flat_memory():
+    """27 recurrent steps over the 81-frame latent: host chunks are copied into fixed device
+    buffers, device memory stays flat, outputs match the oracle on sampled rows and the
+    whole-sequence form bitwise."""
+    cfg = syn.config(4)
+    inp = syn.make_inputs(cfg)
+    B, H, D, Np = cfg.B, cfg.H, cfg.D, cfg.Tc * cfg.HW
+    W = inp["W"].to(DEV)
+    bufs = [torch.empty((B, H, Np, D), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    y_c = torch.empty((B, H, Np, D), dtype=torch.float32, device=DEV)
+    rec = ta.Recurrent(B, H, D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, device=DEV)
+    rows = pu.sample_rows(cfg.T, cfg.HW, cfg.Tc, per_edge=6, n_random=16, seed=4)
+    rows_by_chunk = {}
+    for r in rows:
+        rows_by_chunk.setdefault(r // Np, []).append(r)
+    host = {n: inp[n].pin_memory() for n in ("q", "k", "v")}
+    got = {}
+    y_host = torch.empty((B, H, Np, D), dtype=torch.float32).pin_memory()
+    streamed = torch.empty((B, H, cfg.N, D), dtype=torch.float32, device=DEV)
+    mem = []
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    for t in range(cfg.n_chunks):
+        r0, r1 = t * Np, (t + 1) * Np
+        for buf, n in zip(bufs, ("q", "k", "v")):
+            buf.copy_(host[n][:, :, r0:r1], non_blocking=True)
+        rec.step(bufs[0], bufs[1], bufs[2], W, out=y_c)
+        streamed[:, :, r0:r1].copy_(y_c)
+        y_host.copy_(y_c)
+        torch.cuda.synchronize()
+        mem.append((torch.cuda.memory_allocated(), torch.cuda.max_memory_allocated()))
+        for r in rows_by_chunk.get(t, []):
+            got[r] = y_host[:, :, r - r0].double().numpy()
+    assert len(set(m[0] for m in mem)) == 1, f"device memory not flat: {mem}"
+    assert len(set(m[1] for m in mem)) == 1, f"peak device memory grew: {mem}"
+    y_rows = np.stack([got[r] for r in rows], axis=2)
+    ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=True, rows=rows)
+    _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + " streamed")
+    del bufs, y_c, rec
+    d, y = _fwd(cfg, inp)
+    assert torch.equal(streamed, y)
