@@ -31,6 +31,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "hybrid-attn tokens/s & TFLOP/s per MI355X at 21×30×52, % of MFMA peak"
+COPY_BYTES = 256 << 20
+KERNEL_SOURCE = os.path.join(ROOT, "hybrid_softmax_linear_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hybrid_attn_bf16_c3_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter summary,
+    or None when that summary was taken on a different kernel source."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 flop/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 
@@ -126,6 +147,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (reference kernel for "
+                         "the FETCH_SIZE / WRITE_SIZE counter scale)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
@@ -145,6 +169,13 @@ def main(argv=None):
           flush=True)
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     q, k, v, W = (inp[n].to(dev) for n in ("q", "k", "v", "W"))
     desc = hs.Desc(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, F=cfg.F, Tc=cfg.Tc, To=cfg.To,
                    dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL)
@@ -241,7 +272,7 @@ def main(argv=None):
         "flop_per_step": total_flop,
         "roofline": {"bound": "mfma", "kernel": "hybrid_attn_bf16_kernel<128>",
                      "achieved": attn_tflops, "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "flop_per_launch": attn_flop, "avg_launch_ms": kern_avg,
                      "launches_timed": launches},
         "cpu_baseline": cpu,
