@@ -96,19 +96,40 @@ __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* st
   }
 }
 
-// S^T block (32 keys x 32 queries) of 32-key block kb of the K tile in LDS.
-__device__ __forceinline__ f32x16 qk_block(const unsigned char* kbuf, int kb, const QRegs& Q,
-                                           int lane) {
+// K fragments (A operand of S^T = K Q^T) of 32-key block kb of the K tile in LDS.
+__device__ __forceinline__ void load_k(bf16x8 (&kf)[8], const unsigned char* kbuf, int kb,
+                                       int lane) {
+  const int arow = 32 * kb + kappa(lane & 31);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kf[s] = as_bf16x8(lds_read16(kbuf, ktile_off(arow, 2 * s + (lane >> 5))));
+}
+
+// V^T fragments (A operand of O^T += V^T P^T) of 32-key block kb of the V^T tile in LDS.
+__device__ __forceinline__ void load_v(bf16x8 (&vf)[4][2], const unsigned char* vbuf, int kb,
+                                       int lane) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      vf[db][j] = as_bf16x8(lds_read16(vbuf, vt128_off(32 * db + (lane & 31), 4 * kb + 2 * j + (lane >> 5))));
+}
+
+// S^T block (32 keys x 32 queries) from K fragments.
+__device__ __forceinline__ f32x16 qk_mfma(const bf16x8 (&kf)[8], const QRegs& Q) {
   f32x16 S;
 #pragma unroll
   for (int i = 0; i < 16; ++i) S[i] = 0.0f;
-  const int arow = 32 * kb + kappa(lane & 31);
-  bf16x8 av[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) av[s] = as_bf16x8(lds_read16(kbuf, ktile_off(arow, 2 * s + (lane >> 5))));
-#pragma unroll
-  for (int s = 0; s < 8; ++s) S = mfma32(av[s], Q.op[s], S);
-  // all eight K fragments in flight before the first MFMA waits on one
+  for (int s = 0; s < 8; ++s) S = mfma32(kf[s], Q.op[s], S);
+  return S;
+}
+
+// S^T block of 32-key block kb, all eight K fragments in flight before the first MFMA.
+__device__ __forceinline__ f32x16 qk_block(const unsigned char* kbuf, int kb, const QRegs& Q,
+                                           int lane) {
+  bf16x8 kf[8];
+  load_k(kf, kbuf, kb, lane);
+  f32x16 S = qk_mfma(kf, Q);
   __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   return S;
@@ -147,20 +168,11 @@ __device__ __forceinline__ void softmax_block(bf16x8 (&P)[2], float& l, const f3
   l += acc;
 }
 
-__device__ __forceinline__ void pv_block(Acc& A, const bf16x8 (&P)[2], const unsigned char* vbuf,
-                                         int kb, int lane) {
-  bf16x8 av[4][2];
+__device__ __forceinline__ void pv_mfma(Acc& A, const bf16x8 (&vf)[4][2], const bf16x8 (&P)[2]) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      av[db][j] = as_bf16x8(lds_read16(vbuf, vt128_off(32 * db + (lane & 31), 4 * kb + 2 * j + (lane >> 5))));
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) A.O[db] = mfma32(av[db][j], P[j], A.O[db]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    for (int db = 0; db < 4; ++db) A.O[db] = mfma32(vf[db][j], P[j], A.O[db]);
 }
 
 // Linear branch: O = a^L^T = S^T phi(Q)^T (bf16 MFMA) and n^L = phi(q).z (full sum over
@@ -263,20 +275,28 @@ __device__ __forceinline__ void scale_linear(Acc& A, float nl, float m0, int lan
 
 // One 128-key tile from LDS: four 32-key blocks of S^T = K Q^T, p = 2^(s*ls - m0),
 // l += sum p, O^T += V^T P^T. The last tile of the window masks keys >= nk.
+// LDS reads run one step ahead of the MFMAs that use them: the next block's K fragments
+// and this block's V^T fragments are requested right after this block's S^T MFMAs, so
+// they arrive while the exponentials are computed.
 template <bool kLastTile>
 __device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned char* stage, int kt,
                                              int nk, const QRegs& Q, float ls, int lane) {
   const unsigned char* kbuf = stage;
   const unsigned char* vbuf = stage + kKBytes;
+  bf16x8 kf[8];
+  load_k(kf, kbuf, 0, lane);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int key0 = kt * kKeys + kb * 32;
     if (kLastTile && key0 >= nk) break;
-    f32x16 S = qk_block(kbuf, kb, Q, lane);
+    f32x16 S = qk_mfma(kf, Q);
+    if (kb < 3) load_k(kf, kbuf, kb + 1, lane);
+    bf16x8 vf[4][2];
+    load_v(vf, vbuf, kb, lane);
     if (kLastTile) mask_block(S, key0, nk, lane);
     bf16x8 P[2];
     softmax_block(P, A.l, S, m0, ls);
-    pv_block(A, P, vbuf, kb, lane);
+    pv_mfma(A, vf, P);
   }
 }
 
