@@ -13,6 +13,16 @@ Tolerances
     same order again. Hence |err| <= 2 * 2^-8 * max|v| (+ 2^-9 * max|y| when y is stored
     as bf16). Typical errors are an order of magnitude below this bound; per-chunk errors
     are reported by every test.
+  * bf16 path, per chunk: max-abs error <= 2^-7 * max|y| over that chunk's rows (+ 2^-9 for
+    bf16 y). The worst-case bound above is loose because the rounding errors of thousands
+    of weights average out: to first order the error of a row is sum_j w_j d_j (v_j - y) /
+    sum_j w_j with independent d_j, |d_j| <= 2^-9. Emulating the kernel's roundings on the
+    full workloads in float64 gives at most 1.5e-3 * max|y| per chunk, while leaving out
+    the overlap frames, folding the overlap into the state (the unamended recurrence),
+    folding one frame too few, or dropping the softmax branch moves y by 1.5e-2 to 1.0 of
+    max|y| in every chunk they touch (at the 320x480 bidirectional workload a dropped
+    softmax branch is 4.5e-4 absolute, invisible under the 3e-2 bar). Asserted by every bf16
+    parity test; the small shapes measure up to 2.3e-3 (fp32 y) and 5.0e-3 (bf16 y).
 """
 from __future__ import annotations
 
@@ -27,6 +37,7 @@ from synthetic import to_f64
 
 F32_BAR = 1e-4
 BF16_BAR = 3e-2
+CHUNK_REL_BAR = 2.0 ** -7
 
 
 def bf16_internal_bar(v, y_ref: np.ndarray, y_bf16: bool) -> float:
@@ -36,6 +47,15 @@ def bf16_internal_bar(v, y_ref: np.ndarray, y_bf16: bool) -> float:
     if y_bf16:
         bar += 2.0 ** -9 * float(np.abs(y_ref).max())
     return bar
+
+
+def chunk_rel_bar(y_bf16: bool) -> float:
+    return CHUNK_REL_BAR + (2.0 ** -9 if y_bf16 else 0.0)
+
+
+def chunk_rel_errors(errs: List[Dict[str, float]]) -> List[float]:
+    """Per-chunk max-abs error in units of that chunk's max|y|."""
+    return [e["max_abs"] / max(e["max_ref"], 1e-30) for e in errs]
 
 
 def oracle_rows(inp: Dict[str, torch.Tensor], *, HW: int, Tc: int, To: int, causal: bool,
@@ -86,5 +106,5 @@ def chunk_errors(y: np.ndarray, ref: np.ndarray, rows: Sequence[int], T: int, HW
 
 
 def describe(errs: List[Dict[str, float]]) -> str:
-    return "; ".join(f"t{e['chunk']}: max {e['max_abs']:.2e} rms {e['rms']:.1e} |y| {e['max_ref']:.2f}"
-                     for e in errs)
+    return "; ".join(f"t{e['chunk']}: max {e['max_abs']:.2e} ({e['max_abs'] / max(e['max_ref'], 1e-30):.1e} "
+                     f"of |y|) rms {e['rms']:.1e} |y| {e['max_ref']:.3f}" for e in errs)

@@ -29,6 +29,8 @@ def _check_rows(y_rows, ref, inp, cfg, rows, label):
     assert np.isfinite(y_rows).all()
     assert err <= pu.BF16_BAR
     assert err <= bar
+    rel = pu.chunk_rel_errors(errs)
+    assert max(rel) <= pu.chunk_rel_bar(False), f"per-chunk relative errors {rel}"
 
 
 def _fwd(cfg, inp):

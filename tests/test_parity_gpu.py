@@ -56,12 +56,15 @@ def _check(y, ref, inp, *, bf16, y_bf16, T, HW, Tc, rows=None, label=""):
     rows = list(range(T * HW)) if rows is None else rows
     errs = pu.chunk_errors(y, ref, rows, T, HW, Tc)
     err = max(e["max_abs"] for e in errs)
-    print(f"[{label}] {pu.describe(errs)}", flush=True)
+    rel = max(pu.chunk_rel_errors(errs))
+    print(f"[{label}] max-abs {err:.3e}, max per-chunk relative {rel:.2e}; {pu.describe(errs)}",
+          flush=True)
     assert np.isfinite(y).all()
     if bf16:
         assert err <= pu.BF16_BAR, f"max-abs {err:.3e} > {pu.BF16_BAR}"
         bar = pu.bf16_internal_bar(to_f64(inp["v"]), ref, y_bf16)
         assert err <= bar, f"max-abs {err:.3e} > internal bar {bar:.3e}"
+        assert rel <= pu.chunk_rel_bar(y_bf16), f"per-chunk relative {rel:.3e}"
     else:
         assert err <= pu.F32_BAR, f"max-abs {err:.3e} > {pu.F32_BAR}"
     return err
