@@ -33,6 +33,9 @@ hipError_t launch_gather_window_bf16(const void* ka, const void* va, int64_t a_r
 hipError_t launch_copy_rows(const void* sk, const void* sv, void* dk, void* dv, int64_t src_rows,
                             int64_t src_row0, int64_t rows, int row_bytes, int BH,
                             hipStream_t stream);
+hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH,
+                                     int F, void* img, int64_t img_bh, int64_t img_t,
+                                     const void* W, int nW, void* wimg, hipStream_t stream);
 }  // namespace rehyat
 
 using namespace rehyat;
@@ -174,6 +177,14 @@ size_t fwd_vt_bytes(const rehyat_desc* d) {
 }
 
 // streaming form: the window (tail + chunk) is gathered into K [nk_max][D] and V^T [D][ld]
+// bf16 path: images of the linear-branch operands in the attention kernel's LDS layout,
+// F*256 bytes per state (S^T) and per W (W^T).
+size_t image_bytes(const rehyat_desc* d) { return (size_t)d->F * 256; }
+size_t w_images_bytes(const rehyat_desc* d) {
+  if (d->dtype != REHYAT_BF16) return 0;
+  return (size_t)(d->w_per_head ? d->H : 1) * image_bytes(d);
+}
+
 int64_t step_nk_max(const rehyat_desc* d) { return (int64_t)(d->Tc + d->To) * d->HW; }
 int64_t step_vt_ld(const rehyat_desc* d) { return round_up(step_nk_max(d), 64); }
 size_t step_gather_bytes(const rehyat_desc* d) {
@@ -273,7 +284,10 @@ rehyat_status rehyat_state_update(const rehyat_desc* d, const void* k, const voi
 size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* d) {
   if (check_desc(d) != REHYAT_OK) return 0;
   const size_t BH = (size_t)d->B * d->H;
-  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + fwd_vt_bytes(d);
+  const size_t imgs = (d->dtype == REHYAT_BF16 && n_chunks(d) > 1)
+                          ? BH * n_chunks(d) * image_bytes(d) + w_images_bytes(d) : 0;
+  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + fwd_vt_bytes(d) +
+         imgs;
 }
 
 rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
@@ -304,6 +318,8 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   float* part = reinterpret_cast<float*>(ws);              // [BH][T][E]
   float* states = part + (size_t)BH * d->T * E;             // [BH][nch][E]
   void* vt = states + (size_t)BH * nch * E;                  // V^T (bf16 path)
+  unsigned char* simg = reinterpret_cast<unsigned char*>(vt) + fwd_vt_bytes(d);   // S^T images
+  unsigned char* wimg = simg + (size_t)BH * nch * image_bytes(d);                 // W^T images
   const float us = 1.0f / std::sqrt((float)d->D);
   const bool need_state = nch > 1;   // a single chunk has an empty linear set in both modes
   const bool bf16 = d->dtype == REHYAT_BF16;
@@ -326,6 +342,12 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
     e = launch_scan_states(part, states, d->F, d->D, d->T, d->Tc, d->To, nch,
                            d->mode == REHYAT_BIDIR, BH, s);
     if (e != hipSuccess) return hip_status(e, "state scan launch");
+    if (bf16) {
+      e = launch_linear_images_bf16(states, (int64_t)nch * E, (int64_t)E, nch, BH, d->F, simg,
+                                    (int64_t)(nch * image_bytes(d)), (int64_t)image_bytes(d), Wq,
+                                    d->w_per_head ? d->H : 1, wimg, s);
+      if (e != hipSuccess) return hip_status(e, "linear image launch");
+    }
   }
 
   AttnArgs a{};
@@ -348,6 +370,8 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   a.Wq = Wq; a.w_per_head = d->w_per_head;
   a.S = states; a.z = states + (size_t)d->F * d->D;
   a.s_bh = (int64_t)nch * E; a.s_t = (int64_t)E; a.z_bh = a.s_bh; a.z_t = a.s_t;
+  a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
+  a.st_img = simg; a.st_img_bh = (int64_t)(nch * image_bytes(d)); a.st_img_t = (int64_t)image_bytes(d);
   a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
   a.n_chunks = nch; a.chunk0 = 0; a.step = 0;
   a.bidir = d->mode == REHYAT_BIDIR;
@@ -361,7 +385,10 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
 
 size_t rehyat_recurrent_step_workspace(const rehyat_desc* d) {
   if (check_desc(d) != REHYAT_OK) return 0;
-  return (size_t)d->B * d->H * d->Tc * state_elems(d) * sizeof(float) + step_gather_bytes(d);
+  const size_t imgs = (d->dtype == REHYAT_BF16)
+                          ? (size_t)d->B * d->H * image_bytes(d) + w_images_bytes(d) : 0;
+  return (size_t)d->B * d->H * d->Tc * state_elems(d) * sizeof(float) + step_gather_bytes(d) +
+         imgs;
 }
 
 rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void* q_c,
@@ -419,6 +446,18 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
     uint16_t* kwin = reinterpret_cast<uint16_t*>(part + (size_t)BH * d->Tc * state_elems(d));
     uint16_t* vtwin = kwin + (size_t)BH * step_nk_max(d) * d->D;
     const int64_t ld = step_vt_ld(d);
+    // images of the carried state S^T and of W^T for the linear branch
+    unsigned char* simg = reinterpret_cast<unsigned char*>(part + (size_t)BH * d->Tc * state_elems(d)) +
+                          step_gather_bytes(d);
+    unsigned char* wimg = simg + (size_t)BH * image_bytes(d);
+    if (t > 0) {
+      hipError_t ei = launch_linear_images_bf16(S, (int64_t)d->F * d->D, 0, 1, BH, d->F, simg,
+                                                (int64_t)image_bytes(d), 0, Wq,
+                                                d->w_per_head ? d->H : 1, wimg, s);
+      if (ei != hipSuccess) return hip_status(ei, "linear image launch");
+    }
+    a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
+    a.st_img = simg; a.st_img_bh = (int64_t)image_bytes(d); a.st_img_t = 0;
     hipError_t e = launch_gather_window_bf16(a.ka, a.va, a.a_rows, a.a_rows - tail_in, k_c, v_c,
                                              crow, tail_in, tail_in + crow, 1, 0, 0, 0, vtwin, ld,
                                              kwin, step_nk_max(d), BH, s);

@@ -37,9 +37,11 @@ constexpr int NT = NW * 64;     // threads per workgroup
 constexpr int QT = NW * QW;     // queries per workgroup
 constexpr float kNegBig = -3.0e38f;
 constexpr int kKeys = 128;                               // keys per LDS tile
-constexpr int kKBytes = kKeys * 256;                     // K tile [128 keys][128 d] bf16
-constexpr int kVBytes = kKeys * 256;                     // V^T tile [128 d][128 keys] bf16
-constexpr int kStageBytes = kKBytes + kVBytes;           // 64 KB per stage
+constexpr int kRow = 272;                                // LDS row: 256 B of data + 16 B pad
+constexpr int kDmaInsts = kKeys * (kRow / 16) / 64;      // 1 KB DMA instructions per tile (34)
+constexpr int kKBytes = kKeys * kRow;                    // K tile [128 keys][128 d] bf16
+constexpr int kVBytes = kKeys * kRow;                    // V^T tile [128 d][128 keys] bf16
+constexpr int kStageBytes = kKBytes + kVBytes;           // 68 KB per stage
 constexpr int kBufRsrcWord3 = 0x00020000;                // gfx9 buffer descriptor word 3
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -70,48 +72,56 @@ struct Src {
 };
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }   // vmcnt(0) lgkmcnt(0)
 
-// V^T tile layout: row d (256 B = 128 keys), 16-byte chunk c (keys 8c..8c+7) stored at
-// chunk c ^ (d & 15), so 16 consecutive d rows read at one logical chunk hit 16 distinct
-// bank groups.
-__device__ __forceinline__ int vt128_off(int d, int c) { return d * 256 + ((c ^ (d & 15)) << 4); }
+// Tile layout in LDS (K tile and V^T tile alike): row r (a key for K, a d for V^T) of
+// 256 B at r * 272, its 16-byte chunk c at + 16 c. The 16-byte pad shifts consecutive rows
+// by four banks, so the 16 lanes of a read group (16 consecutive rows, one chunk) cover all
+// 64 banks, and every fragment read below is one per-lane base plus a constant offset.
 
-// Issue the direct-to-LDS loads of tile kt into one stage (4 + 4 per thread). Each
-// instruction writes 1 KB of LDS contiguously (lane i -> bytes 16i..16i+15), so the
-// swizzles are applied by choosing which global chunk each lane fetches.
+// Issue the direct-to-LDS loads of tile kt into one stage. Each instruction writes 64
+// consecutive 16-byte slots (1 KB) of a tile; slot u holds row u / 17, chunk u % 17, and
+// the pad slot (chunk 16) takes a second copy of chunk 0. 34 instructions per tile, spread
+// over the 8 waves.
 __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* stage, int wave,
                                          int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int it = wave * 4 + i;
-    const int r = 4 * it + (lane >> 4);         // K row / V^T row of this lane
-    const int pc = lane & 15;                   // physical chunk
-    const int ck = pc ^ kappa(r & 15);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, (lds_void*)(stage + it * 1024), 16,
-                                             (kt * kKeys + r) * 256 + ck * 16, 0, 0, 0);
-    const int cv = pc ^ (r & 15);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        s.vt, (lds_void*)(stage + kKBytes + it * 1024), 16,
-        r * s.vt_ld_bytes + s.vt_key0_bytes + (kt * kKeys + 8 * cv) * 2, 0, 0, 0);
+  for (int i = 0; i < (kDmaInsts + NW - 1) / NW; ++i) {
+    const int j = wave + NW * i;
+    if (j < kDmaInsts) {
+      const int u = 64 * j + lane;
+      const int r = u / 17;
+      int c = u - 17 * r;
+      c = c == 16 ? 0 : c;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, (lds_void*)(stage + j * 1024), 16,
+                                               (kt * kKeys + r) * 256 + c * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          s.vt, (lds_void*)(stage + kKBytes + j * 1024), 16,
+          r * s.vt_ld_bytes + s.vt_key0_bytes + (kt * kKeys + 8 * c) * 2, 0, 0, 0);
+    }
   }
 }
 
-// K fragments (A operand of S^T = K Q^T) of 32-key block kb of the K tile in LDS.
+// K fragments (A operand of S^T = K Q^T) of 32-key block kb: lane l takes key row
+// 32 kb + kappa(l % 32) (the row order that makes the S^T accumulator the B operand of the
+// PV product) at chunks 2 s + l / 32.
 __device__ __forceinline__ void load_k(bf16x8 (&kf)[8], const unsigned char* kbuf, int kb,
                                        int lane) {
-  const int arow = 32 * kb + kappa(lane & 31);
+  const int base = kappa(lane & 31) * kRow + (lane >> 5) * 16;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) kf[s] = as_bf16x8(lds_read16(kbuf, ktile_off(arow, 2 * s + (lane >> 5))));
+  for (int s = 0; s < 8; ++s) kf[s] = as_bf16x8(lds_read16(kbuf, base + kb * 32 * kRow + s * 32));
 }
 
-// V^T fragments (A operand of O^T += V^T P^T) of 32-key block kb of the V^T tile in LDS.
+// V^T fragments (A operand of O^T += V^T P^T) of 32-key block kb: lane l takes d row
+// 32 db + l % 32 at key chunk 4 kb + 2 j + l / 32.
 __device__ __forceinline__ void load_v(bf16x8 (&vf)[4][2], const unsigned char* vbuf, int kb,
                                        int lane) {
+  const int base = (lane & 31) * kRow + (lane >> 5) * 16;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      vf[db][j] = as_bf16x8(lds_read16(vbuf, vt128_off(32 * db + (lane & 31), 4 * kb + 2 * j + (lane >> 5))));
+      vf[db][j] = as_bf16x8(lds_read16(vbuf, base + db * 32 * kRow + kb * 64 + j * 32));
 }
 
 // S^T block (32 keys x 32 queries) from K fragments.
@@ -176,77 +186,98 @@ __device__ __forceinline__ void pv_mfma(Acc& A, const bf16x8 (&vf)[4][2], const 
 }
 
 // Linear branch: O = a^L^T = S^T phi(Q)^T (bf16 MFMA) and n^L = phi(q).z (full sum over
-// the lane pair). Uses smem as W^T / S^T staging; ends with a barrier.
+// the lane pair). The W^T and S^T slabs of FS features come from bf16 images already in
+// the LDS layout (W^T rows f at chunk c ^ kappa(f & 15); S^T rows d at chunk
+// c ^ (d mod FS/8)) and are copied into `stage` (64 KB) by direct-to-LDS loads. Ends with a
+// barrier.
 template <int F>
 __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs& a,
-                                              const Geo& g, const QRegs& Q, unsigned char* smem,
+                                              const Geo& g, const QRegs& Q, unsigned char* stage,
                                               float* zs, int tid, int lane) {
-  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.Wq) +
-                      (a.w_per_head ? (int64_t)g.h * kDim * F : 0);
-  const float* S = a.S + g.bh * a.s_bh + g.t_local * a.s_t;
+  const int wave = tid >> 6;
   const float* z = a.z + g.bh * a.z_bh + g.t_local * a.z_t;
   float nl = 0.0f;
   for (int f = tid; f < F; f += NT) zs[f] = z[f];
   constexpr int FS = F < 128 ? F : 128;   // features per LDS slab
+  constexpr int NFB = FS / 32;            // 32-feature blocks per slab
   constexpr int NCH = FS / 8;             // 16-byte chunks per S^T row
-  unsigned char* wt = smem;               // [FS][128] bf16, K-tile layout
-  unsigned char* st = smem + 32768;       // [128 d][FS] bf16
+  constexpr int SLAB = FS * 256;          // bytes of one W^T slab and of one S^T slab
+  const unsigned char* wimg = reinterpret_cast<const unsigned char*>(a.wt_img) +
+                              (a.w_per_head ? (int64_t)g.h * a.wt_img_head : 0);
+  const unsigned char* simg = reinterpret_cast<const unsigned char*>(a.st_img) +
+                              g.bh * a.st_img_bh + g.t_local * a.st_img_t;
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wimg, (short)0, F * 256, kBufRsrcWord3);
+  const __amdgpu_buffer_rsrc_t sr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)simg, (short)0, F * 256, kBufRsrcWord3);
+  unsigned char* wt = stage;              // [FS][128] bf16
+  unsigned char* st = stage + 32768;      // [128 d][FS] bf16
 #pragma unroll 1
   for (int f0 = 0; f0 < F; f0 += FS) {
     if (f0 > 0) __syncthreads();
-    if (tid < 256) stage_wt(wt, W, F, f0, FS, tid);   // stage_wt is written for 256 threads
-    // S^T slab: thread reads S[f][4*d4 .. +4] (fp32) and scatters 4 bf16 into column f.
-    for (int id = tid; id < FS * 32; id += NT) {
-      const int fl = id % FS, d4 = id / FS;
-      f32x4 v = *reinterpret_cast<const f32x4*>(S + (int64_t)(f0 + fl) * kDim + 4 * d4);
+    const int base = (f0 / FS) * SLAB;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 4 * d4 + e;
-        *reinterpret_cast<bf16*>(st + d * (FS * 2) + ((((fl >> 3) ^ (d & (NCH - 1)))) << 4) +
-                                 ((fl & 7) << 1)) = (bf16)v[e];
+    for (int i = 0; i < (SLAB / 1024 + NW - 1) / NW; ++i) {
+      const int j = wave + NW * i;
+      if (j < SLAB / 1024) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wt + j * 1024), 16,
+                                                 base + j * 1024 + lane * 16, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(st + j * 1024), 16,
+                                                 base + j * 1024 + lane * 16, 0, 0, 0);
       }
     }
+    wait_vmem();
     __syncthreads();
-#pragma unroll 1
-    for (int fb = 0; fb < FS / 32; ++fb) {
-      // U^T block: rows = features 32fb + kappa(l%32) (A = W^T), cols = queries (B = Q^T)
-      f32x16 U;
+    // U^T blocks: rows = features 32fb + kappa(l%32) (A = W^T), cols = queries (B = Q^T);
+    // G chains at a time (fewer for F = 256, whose slab loop keeps more state live).
+    constexpr int G = F > 128 ? 2 : NFB;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) U[i] = 0.0f;
-      const int arow = 32 * fb + kappa(lane & 31);
+    for (int fg = 0; fg < NFB; fg += G) {
+      f32x16 U[G];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x8 av = as_bf16x8(lds_read16(wt, ktile_off(arow, 2 * s + (lane >> 5))));
-        U = mfma32(av, Q.op[s], U);
-      }
-      // phi = 1 + u + u^2/2, rounded to bf16: B operand of a^L^T = S^T phi^T.
-      bf16x8 P[2];
+      for (int k = 0; k < G; ++k)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 pk;
+        for (int i = 0; i < 16; ++i) U[k][i] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i0 = 8 * j + 2 * e;
-          float u0 = U[i0] * a.u_scale, u1 = U[i0 + 1] * a.u_scale;
-          float p0 = 1.0f + u0 + 0.5f * u0 * u0;
-          float p1 = 1.0f + u1 + 0.5f * u1 * u1;
-          unsigned w = pack_bf16_u32(p0, p1);
-          pk[e] = w;
-          const int f = f0 + 32 * fb + cidx(i0, lane);
-          nl += bf16_lo(w) * zs[f] + bf16_hi(w) * zs[f + 1];
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          const int arow = 32 * (fg + k) + kappa(lane & 31);
+          bf16x8 av = as_bf16x8(lds_read16(wt, ktile_off(arow, 2 * s + (lane >> 5))));
+          U[k] = mfma32(av, Q.op[s], U[k]);
         }
-        P[j] = as_bf16x8(pk);
-      }
+      // phi = 1 + u + u^2/2, rounded to bf16: B operand of a^L^T = S^T phi^T.
+      bf16x8 P[G][2];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = 32 * db + (lane & 31);
+      for (int k = 0; k < G; ++k)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int c = 4 * fb + 2 * j + (lane >> 5);
-          bf16x8 av = as_bf16x8(lds_read16(st, d * (FS * 2) + ((c ^ (d & (NCH - 1))) << 4)));
-          A.O[db] = mfma32(av, P[j], A.O[db]);
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i0 = 8 * j + 2 * e;
+            float u0 = U[k][i0] * a.u_scale, u1 = U[k][i0 + 1] * a.u_scale;
+            float p0 = 1.0f + u0 + 0.5f * u0 * u0;
+            float p1 = 1.0f + u1 + 0.5f * u1 * u1;
+            unsigned w = pack_bf16_u32(p0, p1);
+            pk[e] = w;
+            const int f = f0 + 32 * (fg + k) + cidx(i0, lane);
+            nl += bf16_lo(w) * zs[f] + bf16_hi(w) * zs[f + 1];
+          }
+          P[k][j] = as_bf16x8(pk);
         }
-      }
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = 32 * db + (lane & 31);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int c = 4 * (fg + k) + 2 * j + (lane >> 5);
+            bf16x8 av = as_bf16x8(lds_read16(st, d * (FS * 2) + ((c ^ (d & (NCH - 1))) << 4)));
+            A.O[db] = mfma32(av, P[k][j], A.O[db]);
+          }
+        }
     }
   }
   nlf = pair_sum(nl);
@@ -275,28 +306,47 @@ __device__ __forceinline__ void scale_linear(Acc& A, float nl, float m0, int lan
 
 // One 128-key tile from LDS: four 32-key blocks of S^T = K Q^T, p = 2^(s*ls - m0),
 // l += sum p, O^T += V^T P^T. The last tile of the window masks keys >= nk.
-// LDS reads run one step ahead of the MFMAs that use them: the next block's K fragments
-// and this block's V^T fragments are requested right after this block's S^T MFMAs, so
-// they arrive while the exponentials are computed.
+// LDS reads run one block ahead of the MFMAs that use them: kf and vf hold block 0's K and
+// V^T fragments on entry, and each block requests the next block's fragments right after
+// its S^T MFMAs, so they arrive while the exponentials and PV MFMAs run. In a tile that is
+// not the window's last, the barrier that hands over the next stage sits inside block 3:
+// once this wave's reads of the current stage have returned and its share of the next
+// tile has landed, the barrier passes and the next tile's block-0 fragments are requested
+// before block 3's exponentials (kf and vf hold them on exit), so the pipeline does not
+// drain at tile boundaries.
 template <bool kLastTile>
-__device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned char* stage, int kt,
-                                             int nk, const QRegs& Q, float ls, int lane) {
+__device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned char* stage,
+                                             const unsigned char* next_stage, int kt, int nk,
+                                             const QRegs& Q, float ls, int lane,
+                                             bf16x8 (&kf)[8], bf16x8 (&vf)[4][2]) {
   const unsigned char* kbuf = stage;
   const unsigned char* vbuf = stage + kKBytes;
-  bf16x8 kf[8];
-  load_k(kf, kbuf, 0, lane);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int key0 = kt * kKeys + kb * 32;
     if (kLastTile && key0 >= nk) break;
     f32x16 S = qk_mfma(kf, Q);
-    if (kb < 3) load_k(kf, kbuf, kb + 1, lane);
-    bf16x8 vf[4][2];
-    load_v(vf, vbuf, kb, lane);
+    bf16x8 vn[4][2];
+    if (kb < 3) {
+      load_k(kf, kbuf, kb + 1, lane);
+      load_v(vn, vbuf, kb + 1, lane);
+    } else if (!kLastTile) {
+      wait_vmem_lds();
+      __syncthreads();
+      load_k(kf, next_stage, 0, lane);
+      load_v(vn, next_stage + kKBytes, 0, lane);
+    }
     if (kLastTile) mask_block(S, key0, nk, lane);
     bf16x8 P[2];
     softmax_block(P, A.l, S, m0, ls);
     pv_mfma(A, vf, P);
+    if (kb < 3 || !kLastTile) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        vf[db][0] = vn[db][0];
+        vf[db][1] = vn[db][1];
+      }
+    }
   }
 }
 
@@ -324,32 +374,41 @@ __device__ __forceinline__ float max_sweep(const Src& src, const QRegs& Q, unsig
 }
 
 // The key loop over a window whose tile 0 is already in stage 0: double-buffered
-// direct-to-LDS tiles, the last tile peeled (masking).
-// Waves whose 32 query rows all lie past the chunk (ragged last query tile) only help
-// with the tile loads and barriers.
+// direct-to-LDS tiles, one barrier per tile, the last tile peeled (masking).
+// Waves without a query tile (in workgroups that hold 7 of the chunk's wave tiles) only
+// help with the tile loads and barriers.
 __device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const QRegs& Q,
                                          unsigned char* smem, float ls, int wave, int lane,
                                          bool active) {
   const int nk = src.nk;
   const int ntiles = (nk + kKeys - 1) / kKeys;
+  bf16x8 kf[8], vf[4][2];
+  if (active) {
+    load_k(kf, smem, 0, lane);
+    load_v(vf, smem + kKBytes, 0, lane);
+  }
 #pragma unroll 1
   for (int kt = 0; kt < ntiles - 1; ++kt) {
     unsigned char* cur = smem + (kt & 1) * kStageBytes;
     unsigned char* nxt = smem + ((kt & 1) ^ 1) * kStageBytes;
     tile_dma(src, kt + 1, nxt, wave, lane);
-    if (active) process_tile<false>(A, m0, cur, kt, nk, Q, ls, lane);
-    wait_vmem();
-    __syncthreads();
+    if (active) {
+      process_tile<false>(A, m0, cur, nxt, kt, nk, Q, ls, lane, kf, vf);
+    } else {
+      wait_vmem_lds();
+      __syncthreads();
+    }
   }
   const int kt = ntiles - 1;
-  if (active) process_tile<true>(A, m0, smem + (kt & 1) * kStageBytes, kt, nk, Q, ls, lane);
+  if (active)
+    process_tile<true>(A, m0, smem + (kt & 1) * kStageBytes, smem, kt, nk, Q, ls, lane, kf, vf);
   __syncthreads();
 }
 
-// Load window tile 0 into stage 0 and fix the reference: max(mlow, block-0 row maximum).
+// Wait for window tile 0 in stage 0 (its loads were issued by the caller) and fix the
+// reference: max(mlow, block-0 row maximum).
 __device__ __forceinline__ float start_window(float mlow, const Src& src, const QRegs& Q,
                                               unsigned char* smem, float ls, int wave, int lane) {
-  tile_dma(src, 0, smem, wave, lane);
   wait_vmem();
   __syncthreads();
   f32x16 S = qk_block(smem, 0, Q, lane);
@@ -361,7 +420,7 @@ template <int F>
 __global__ void __launch_bounds__(NT)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 hybrid_attn_bf16_kernel(AttnArgs a) {
-  // 128 KB: two K/V^T stages during the key loop; W^T and S^T slabs for the linear branch.
+  // 136 KB: two K/V^T stages during the key loop; W^T and S^T slabs for the linear branch.
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
   __shared__ float zs[F];
   __shared__ int bad_flag;
@@ -385,7 +444,13 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   g.lo = (c0 - (int64_t)a.To * a.HW) > 0 ? (c0 - (int64_t)a.To * a.HW) : 0;
   g.hi = c0 + g.rows;
   g.has_linear = a.bidir ? (g.lo > 0 || g.hi < N) : (g.lo > 0);
-  g.q_wave0 = qt * QT + wave * QW;
+  // The chunk's 32-query wave tiles are split evenly over its workgroups (7 or 8 per
+  // workgroup), so no workgroup holds a mostly idle last tile.
+  const int ntile_c = (g.t_local == a.n_chunks - 1) ? a.tiles_last : a.tiles_per_chunk;
+  const int nwt = (g.rows + QW - 1) / QW;
+  const int wt0 = (qt * nwt) / ntile_c, wt1 = ((qt + 1) * nwt) / ntile_c;
+  const bool active = wt0 + wave < wt1;   // wave-uniform
+  g.q_wave0 = (wt0 + wave) * QW;
   g.q_row_base = a.step ? 0 : c0;   // row of the chunk start in the q buffer
   if (tid == 0) bad_flag = 0;
 
@@ -394,7 +459,7 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   const int qrow = g.q_wave0 + (lane & 31);
   QRegs Q;
   {
-    const bool ok = qrow < g.rows;
+    const bool ok = active && qrow < g.rows;
     const uint16_t* src = qh + (g.q_row_base + (ok ? qrow : 0)) * kDim + 8 * (lane >> 5);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -421,16 +486,18 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   const float ls = a.logit_scale;
 
   // ---- linear branch, reference m0, key loop ------------------------------------------
+  // Window tile 0 streams into stage 0 while the linear branch stages its operands in
+  // stage 1.
+  tile_dma(src, 0, smem, wave, lane);
   Acc A;
   float nl = 1.0f, ml = kNegBig;
   zero_acc(A);
   if (g.has_linear) {
-    linear_branch<F>(A, nl, a, g, Q, smem, zs, tid, lane);
+    linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane);
     ml = fast_log2(nl);
   }
   float m0 = start_window(ml, src, Q, smem, ls, wave, lane);
   if (g.has_linear) scale_linear(A, nl, m0, lane);
-  const bool active = g.q_wave0 < g.rows;   // wave-uniform
   key_loop(A, m0, src, Q, smem, ls, wave, lane, active);
 
   // ---- overflow guard: recompute the workgroup with the exact row maxima ---------------
@@ -445,7 +512,8 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
     if (bad_flag) {
       const float mx = max_sweep(src, Q, smem, ls, wave, lane);
       zero_acc(A);
-      if (g.has_linear) linear_branch<F>(A, nl, a, g, Q, smem, zs, tid, lane);
+      tile_dma(src, 0, smem, wave, lane);
+      if (g.has_linear) linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane);
       // reference = the exact maximum over the linear weight and every window key: every
       // p <= 1 and l >= 1
       m0 = start_window(fmaxf(ml, mx), src, Q, smem, ls, wave, lane);
@@ -456,7 +524,7 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue: y = O / l ------------------------------------------------------------
   const float inv = 1.0f / pair_sum(A.l);
-  if (qrow < g.rows) {
+  if (active && qrow < g.rows) {
     const int64_t off = head_off(g.bh, a.q_rows, kDim) + (g.q_row_base + qrow) * kDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {

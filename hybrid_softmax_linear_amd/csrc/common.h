@@ -133,6 +133,10 @@ struct AttnArgs {
   const float* S;       // linear state of (head, chunk): S + bh*s_bh + t*s_t, [F, D]
   const float* z;       //                                 z + bh*z_bh + t*z_t, [F]
   int64_t s_bh, s_t, z_bh, z_t;
+  // bf16 path: images of W^T (head h at wt_img + h*wt_img_head bytes) and of S^T (state
+  // (bh, t) at st_img + bh*st_img_bh + t*st_img_t bytes) in the LDS slab layout
+  const void* wt_img; int64_t wt_img_head;
+  const void* st_img; int64_t st_img_bh, st_img_t;
   int H;
   int HW, Tc, To, T;    // geometry of the whole video
   int n_chunks;         // chunks handled by this launch

@@ -278,6 +278,57 @@ gather_window_bf16_kernel(const uint16_t* ka, const uint16_t* va, int64_t a_rows
   }
 }
 
+// bf16 images of the linear-branch operands of the attention kernel, laid out byte for
+// byte as that kernel's LDS slabs, so it can copy them into LDS with direct loads:
+//   S^T image of one state (F x 128 fp32, row f): per slab of FS = min(F, 128) features,
+//     128 rows d of FS bf16; feature chunk c (8 features) of row d sits at chunk
+//     c ^ (d mod FS/8).
+//   W^T image of one W (128 x F bf16, row d): F rows f of 128 bf16; d chunk c of row f
+//     sits at chunk c ^ kappa(f mod 16).
+// st_image: one block transposes S[f0 .. f0+32)[0 .. 128) of state (t, bh) through LDS.
+__global__ void __launch_bounds__(256)
+st_image_kernel(const float* __restrict__ S, int64_t s_bh, int64_t s_t, int F,
+                unsigned char* __restrict__ img, int64_t img_bh, int64_t img_t) {
+  __shared__ float tile[32][kDim + 1];
+  const int f0 = blockIdx.x * 32, t = blockIdx.y, bh = blockIdx.z;
+  const float* src = S + bh * s_bh + t * s_t + (int64_t)f0 * kDim;
+  for (int i = threadIdx.x; i < 32 * kDim; i += 256) tile[i / kDim][i % kDim] = src[i];
+  __syncthreads();
+  const int FS = F < 128 ? F : 128, NCH = FS / 8;
+  const int slab = f0 / FS, fl0 = f0 % FS;
+  unsigned char* dst = img + bh * img_bh + t * img_t + (int64_t)slab * kDim * FS * 2;
+  for (int i = threadIdx.x; i < kDim * 4; i += 256) {
+    const int d = i & (kDim - 1), cc = i >> 7;
+    const int c = (fl0 >> 3) + cc;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16_u32(tile[8 * cc + 2 * e][d], tile[8 * cc + 2 * e + 1][d]);
+    *reinterpret_cast<u32x4*>(dst + d * FS * 2 + ((c ^ (d & (NCH - 1))) << 4)) = w;
+  }
+}
+
+// wt_image: one block writes rows f0 .. f0+32 of the W^T image of head h.
+__global__ void __launch_bounds__(256)
+wt_image_kernel(const uint16_t* __restrict__ W, int F, unsigned char* __restrict__ img) {
+  __shared__ uint16_t tile[kDim][34];
+  const int f0 = blockIdx.x * 32, h = blockIdx.y;
+  const uint16_t* src = W + (int64_t)h * kDim * F;
+  for (int i = threadIdx.x; i < kDim * 32; i += 256) {
+    const int d = i >> 5, fl = i & 31;
+    tile[d][fl] = src[(int64_t)d * F + f0 + fl];
+  }
+  __syncthreads();
+  unsigned char* dst = img + (int64_t)h * F * 256;
+  for (int i = threadIdx.x; i < 32 * 16; i += 256) {
+    const int c = i & 15, fl = i >> 4, f = f0 + fl;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (unsigned)tile[8 * c + 2 * e][fl] | ((unsigned)tile[8 * c + 2 * e + 1][fl] << 16);
+    *reinterpret_cast<u32x4*>(dst + f * 256 + ((c ^ kappa(f & 15)) << 4)) = w;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather_window_bf16(const void* ka, const void* va, int64_t a_rows, int64_t a_row0,
@@ -317,6 +368,26 @@ hipError_t launch_phi_bf16(const void* x, int64_t n, const void* W, int w_per_he
     case 128: hipLaunchKernelGGL(phi_bf16_kernel<128>, grid, block, 0, stream, xx, n, ww, w_per_head, H, out, out_f32, u_scale, tph); break;
     case 256: hipLaunchKernelGGL(phi_bf16_kernel<256>, grid, block, 0, stream, xx, n, ww, w_per_head, H, out, out_f32, u_scale, tph); break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// S^T images of nst states per head (state (bh, t) at S + bh*s_bh + t*s_t, [F][128] fp32)
+// into img + bh*img_bh + t*img_t, and the W^T image of each of nW matrices W ([nW][128][F]
+// bf16) into wimg + h*F*256 (wimg may be null to skip it).
+hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH,
+                                     int F, void* img, int64_t img_bh, int64_t img_t,
+                                     const void* W, int nW, void* wimg, hipStream_t stream) {
+  if (F % 32 != 0) return hipErrorInvalidValue;
+  if (nst > 0) {
+    dim3 grid(F / 32, nst, BH), block(256);
+    hipLaunchKernelGGL(st_image_kernel, grid, block, 0, stream, S, s_bh, s_t, F,
+                       (unsigned char*)img, img_bh, img_t);
+  }
+  if (wimg) {
+    dim3 grid(F / 32, nW), block(256);
+    hipLaunchKernelGGL(wt_image_kernel, grid, block, 0, stream, (const uint16_t*)W, F,
+                       (unsigned char*)wimg);
   }
   return hipGetLastError();
 }

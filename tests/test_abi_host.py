@@ -102,9 +102,15 @@ def test_workspace_sizes():
     E = d.F * d.D + d.F
     BH = d.B * d.H
     vt = BH * d.n_chunks * d.D * 64 * 2   # HW=10: gathered V^T windows of 40 keys, 64-padded
-    assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == BH * (d.T + d.n_chunks) * E * 4 + vt
+    img = d.F * 256                       # one bf16 S^T or W^T image (F rows of 128 d)
+    assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == (
+        BH * (d.T + d.n_chunks) * E * 4 + vt + BH * d.n_chunks * img + img)
     gather = BH * 40 * d.D * 2 + BH * d.D * 64 * 2
-    assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == BH * d.Tc * E * 4 + gather
+    assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == (
+        BH * d.Tc * E * 4 + gather + BH * img + img)
+    dh = _desc(w_per_head=1)              # one W^T image per head
+    assert L.rehyat_recurrent_step_workspace(ctypes.byref(dh.c())) == (
+        BH * d.Tc * E * 4 + gather + BH * img + d.H * img)
     assert L.rehyat_state_update_workspace(ctypes.byref(d.c()), 1000) == BH * 2 * E * 4
     assert L.rehyat_state_update_workspace(ctypes.byref(d.c()), 0) == 0
     assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(_desc(D=64).c())) == 0   # invalid desc
