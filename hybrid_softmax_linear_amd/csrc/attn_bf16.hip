@@ -416,6 +416,51 @@ __device__ __forceinline__ float start_window(float mlow, const Src& src, const 
   return fmaxf(mlow, pair_max(rowmax16(S)) * ls);
 }
 
+// Work order. Blocks are handed to the XCDs round-robin (block b to XCD b mod 8) and each
+// XCD starts its blocks in order as CUs free up. Each XCD first takes its share of the
+// tiles of chunks 1 .. n_chunks-1, then its share of chunk 0's tiles, whose window lacks the
+// overlap frames: the last workgroups to start are the short ones. Within a share an XCD
+// takes consecutive tiles of one window, which then share its L2. Returns (head, chunk
+// within the launch, query tile) of block b.
+__device__ __forceinline__ void tile_of_block(const AttnArgs& a, int b, int& bh, int& t_local,
+                                              int& qt) {
+  const int nb = a.nblocks, nch = a.n_chunks;
+  const int tpc = a.tiles_per_chunk, tl = a.tiles_last;
+  const int BH = nb / a.tiles_per_head;
+  const int ntile0 = nch == 1 ? tl : tpc;
+  const int H = nb - BH * ntile0;                   // tiles of chunks 1 .. nch-1
+  const int x = b & 7, i = b >> 3;
+  const int hq = H >> 3, hr = H & 7;
+  const int hcnt = hq + (x < hr ? 1 : 0);
+  const int hstart = x * hq + (x < hr ? x : hr);
+  int item;
+  if (i < hcnt) {
+    item = hstart + i;
+  } else {
+    const int before = x * (nb >> 3) + (x < (nb & 7) ? x : (nb & 7));   // blocks of XCDs < x
+    item = H + (before - hstart) + (i - hcnt);
+  }
+  if (item < H) {
+    const int mid = (nch - 2) * BH * tpc;           // tiles of chunks 1 .. nch-2
+    if (item < mid) {
+      const int c = item / (BH * tpc), r = item - c * BH * tpc;
+      t_local = c + 1;
+      bh = r / tpc;
+      qt = r - bh * tpc;
+    } else {
+      const int r = item - mid;
+      t_local = nch - 1;
+      bh = r / tl;
+      qt = r - bh * tl;
+    }
+  } else {
+    const int r = item - H;
+    t_local = 0;
+    bh = r / ntile0;
+    qt = r - bh * ntile0;
+  }
+}
+
 template <int F>
 __global__ void __launch_bounds__(NT)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -428,13 +473,9 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int tile = xcd_remap(blockIdx.x, a.nblocks);
-
   Geo g;
-  g.bh = tile / a.tiles_per_head;
-  const int rr = tile - g.bh * a.tiles_per_head;
-  g.t_local = rr / a.tiles_per_chunk;
-  const int qt = rr - g.t_local * a.tiles_per_chunk;
+  int qt;
+  tile_of_block(a, blockIdx.x, g.bh, g.t_local, qt);
   const int t = a.chunk0 + g.t_local;
   g.h = g.bh % a.H;
   const int64_t Np = (int64_t)a.Tc * a.HW;
