@@ -17,6 +17,7 @@ recurrent steps, the bidirectional form, and full softmax attention of the same 
 (one chunk covering the whole sequence) with librehyat and with torch's SDPA.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-context]
+    python bench.py --sweep     (Tc, To) grid of the ablation, one JSON line per entry
 """
 from __future__ import annotations
 
@@ -140,6 +141,50 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+SWEEP_TC = (1, 2, 3, 5, 7)
+SWEEP_TO = (0, 1, 2, 3)
+SWEEP_LATENT = {3: "21x30x52", 2: "21x20x30"}
+
+
+def sweep(args):
+    """(Tc, To) grid of the ablation at two latents, causal, bf16 in / fp32 out."""
+    import torch
+    import synthetic as syn
+    import hybrid_softmax_linear_amd as hs
+    from hybrid_softmax_linear_amd import torch_api as ta
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for ci in (3, 2):
+        cfg = syn.config(ci)
+        inp = syn.make_inputs(cfg)
+        q, k, v, W = (inp[n].to(dev) for n in ("q", "k", "v", "W"))
+        y = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        base = dict(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, F=cfg.F, dtype=hs.BF16,
+                    y_dtype=hs.F32)
+        full = hs.Desc(**base, Tc=cfg.T, To=0, mode=hs.CAUSAL)
+        wsf = ta.workspace(hs.rehyat_hybrid_fwd_workspace(full), dev)
+        full_ms = time_calls(lambda: hs.rehyat_hybrid_fwd(full, q, k, v, W, W, y, wsf, stream=stream),
+                             max(3, args.steps // 4), 2)
+        full_flop = 4 * cfg.D * cfg.N * cfg.N * cfg.B * cfg.H
+        del wsf
+        for Tc in SWEEP_TC:
+            for To in SWEEP_TO:
+                d = hs.Desc(**base, Tc=Tc, To=To, mode=hs.CAUSAL)
+                ws = ta.workspace(hs.rehyat_hybrid_fwd_workspace(d), dev)
+                ms = time_calls(lambda: hs.rehyat_hybrid_fwd(d, q, k, v, W, W, y, ws, stream=stream),
+                                args.steps, args.warmup)
+                flop = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D, cfg.F, Tc, To, causal=True)[0]
+                print(json.dumps({
+                    "sweep": SWEEP_LATENT[ci], "B": cfg.B, "H": cfg.H,
+                    "Tc": Tc, "To": To, "ms": ms, "tokens_per_s": cfg.B * cfg.N / (ms * 1e-3),
+                    "tflops": flop / (ms * 1e-3) / 1e12, "flop": flop,
+                    "full_softmax_ms": full_ms, "full_over_hybrid_flop": full_flop / flop,
+                    "full_over_hybrid_time": full_ms / ms}), flush=True)
+                del ws
+        del q, k, v, W, y
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +192,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the default line: time every (Tc, To) of the pages' "
+                         "ablation grid at the 21x30x52 and 21x20x30 latents next to full "
+                         "softmax, one JSON line per configuration")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (reference kernel for "
                          "the FETCH_SIZE / WRITE_SIZE counter scale)")
@@ -162,6 +211,8 @@ def main(argv=None):
     from hybrid_softmax_linear_amd import torch_api as ta
 
     hs.lib()   # fail loudly if the HIP library is missing
+    if args.sweep:
+        return sweep(args)
     cfg = syn.config(3)
     inp = syn.make_inputs(cfg)
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
