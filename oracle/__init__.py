@@ -15,4 +15,8 @@ from .rehyat_oracle import (  # noqa: F401
     state_direct,
     recurrent_init,
     recurrent_step,
+    EluFeatureMap,
+    PolyMlpFeatureMap,
+    feature,
+    feature_dim,
 )

@@ -33,6 +33,19 @@ the design notes of the repository):
     printed recurrence.
   * No mask inside a chunk: the softmax window is bidirectional, overlap frames included.
   * A last chunk shorter than Tc frames (T not a multiple of Tc) keeps hi = N.
+
+Feature maps. Every function below takes the feature map of the queries and of the keys
+as its Wq / Wk arguments: a D x F matrix W selects the fixed map phi(x) = 1 + u + u^2/2,
+u = x W / sqrt(D) (per head: an [H, D, F] array); a feature-map object (or one per head)
+selects that map. Key design 3 gives two more:
+  * EluFeatureMap: 1 + elu(x), elementwise (F = D), the fixed map of earlier linear
+    attention that the note compares against.
+  * PolyMlpFeatureMap, the learned polynomial map. Reading: the per-head embedding network
+    (grouped 1x1 convolution + nonlinearity; "2-layer MLP" in the hyper-parameters) is
+    psi(x) = relu(x W1 + b1) W2 + b2 with W1 [D, h], W2 [h, F]; the nonlinearity is not
+    named, ReLU is taken. psi is split into P equal parts (degree P = 2 in the note) and
+    part i (1-based) is raised elementwise to the power i: phi = [psi_1, psi_2 * psi_2].
+    This map can give a negative phi(q).phi(k); the definition is used as it stands.
 """
 from __future__ import annotations
 
@@ -43,7 +56,8 @@ import numpy as np
 
 __all__ = [
     "chunk_layout", "phi", "hybrid_attention", "hybrid_attention_bh", "hybrid_recurrent",
-    "state_direct", "recurrent_init", "recurrent_step",
+    "state_direct", "recurrent_init", "recurrent_step", "EluFeatureMap", "PolyMlpFeatureMap",
+    "feature", "feature_dim",
 ]
 
 
@@ -76,6 +90,50 @@ def phi(x: np.ndarray, W: np.ndarray) -> np.ndarray:
     D = x.shape[-1]
     u = (x @ W) / math.sqrt(D)
     return 1.0 + u + 0.5 * u * u
+
+
+class EluFeatureMap:
+    """phi(x) = 1 + elu(x) elementwise: x + 1 for x > 0, exp(x) otherwise (F = D)."""
+
+    def __call__(self, x: np.ndarray) -> np.ndarray:
+        x = np.asarray(x, dtype=np.float64)
+        return np.where(x > 0, 1.0 + x, np.exp(np.minimum(x, 0.0)))
+
+    def dim(self, D: int) -> int:
+        return D
+
+
+class PolyMlpFeatureMap:
+    """Learned polynomial map of key design 3 (reading in the module docstring):
+    psi = relu(x W1 + b1) W2 + b2, phi = [psi part i ** i for i = 1 .. P]."""
+
+    def __init__(self, W1, b1, W2, b2, P: int = 2):
+        self.W1 = np.asarray(W1, dtype=np.float64)
+        self.b1 = np.asarray(b1, dtype=np.float64)
+        self.W2 = np.asarray(W2, dtype=np.float64)
+        self.b2 = np.asarray(b2, dtype=np.float64)
+        self.P = int(P)
+        if self.W2.shape[1] % self.P:
+            raise ValueError("F must split into P equal parts")
+
+    def __call__(self, x: np.ndarray) -> np.ndarray:
+        x = np.asarray(x, dtype=np.float64)
+        hid = np.maximum(x @ self.W1 + self.b1, 0.0)
+        psi = hid @ self.W2 + self.b2
+        parts = np.split(psi, self.P, axis=-1)
+        return np.concatenate([part ** (i + 1) for i, part in enumerate(parts)], axis=-1)
+
+    def dim(self, D: int) -> int:
+        return self.W2.shape[1]
+
+
+def feature(x: np.ndarray, W) -> np.ndarray:
+    """Apply the feature map W (a D x F matrix for the fixed map, or a map object)."""
+    return W(x) if callable(W) else phi(x, W)
+
+
+def feature_dim(W, D: int) -> int:
+    return W.dim(D) if callable(W) else np.asarray(W).shape[1]
 
 
 def _linear_ranges(lo: int, hi: int, N: int, causal: bool) -> List[Tuple[int, int]]:
@@ -112,7 +170,7 @@ def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool
     y = np.empty((rows_arr.size, v.shape[1]), dtype=np.float64)
     nS_out = np.empty(rows_arr.size)
     nL_out = np.empty(rows_arr.size)
-    phik = phi(k, Wk)
+    phik = feature(k, Wk)
     inv_sqrt_d = 1.0 / math.sqrt(D)
     for (row_lo, row_hi, lo, hi) in chunk_layout(T, HW, Tc, To):
         sel = np.nonzero((rows_arr >= row_lo) & (rows_arr < row_hi))[0]
@@ -128,7 +186,7 @@ def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool
             nS = ES.sum(axis=1)
             nL = np.zeros(pos.size)
             if Lr:
-                pq = phi(Qb, Wq)
+                pq = feature(Qb, Wq)
                 for (a, b) in Lr:
                     EL = pq @ phik[a:b].T                   # linear branch weights
                     num = num + EL @ v[a:b]
@@ -141,7 +199,11 @@ def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool
     return y
 
 
-def _w_for_head(W: np.ndarray, h: int) -> np.ndarray:
+def _w_for_head(W, h: int):
+    if callable(W):
+        return W
+    if isinstance(W, (list, tuple)):
+        return W[h]
     W = np.asarray(W)
     return W if W.ndim == 2 else W[h]
 
@@ -185,7 +247,7 @@ def state_direct(k, v, Wk, j_end: int, j_begin: int = 0) -> Tuple[np.ndarray, np
     j in [j_begin, j_end) of phi(k_j) v_j^T (an F x D matrix s) and phi(k_j) (z, length F)."""
     k = np.asarray(k, dtype=np.float64)[j_begin:j_end]
     v = np.asarray(v, dtype=np.float64)[j_begin:j_end]
-    pk = phi(k, Wk)
+    pk = feature(k, Wk)
     return pk.T @ v, pk.sum(axis=0)
 
 
@@ -206,7 +268,7 @@ def hybrid_recurrent(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int,
     N, D = q.shape
     T = N // HW
     layout = chunk_layout(T, HW, Tc, To)
-    F = np.asarray(Wq).shape[1]
+    F = feature_dim(Wq, D)
     s = np.zeros((F, v.shape[1]))
     z = np.zeros(F)
     y = np.empty((N, v.shape[1]))
@@ -218,11 +280,11 @@ def hybrid_recurrent(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int,
         ES = np.exp((Q @ k[lo:hi].T) * inv_sqrt_d)
         aS = ES @ v[lo:hi]
         nS = ES.sum(axis=1)
-        pq = phi(Q, Wq)
+        pq = feature(Q, Wq)
         y[row_lo:row_hi] = (aS + pq @ s) / (nS + pq @ z)[:, None]
         lo_next = layout[t + 1][2] if t + 1 < len(layout) else lo
         if lo_next > lo:
-            pk = phi(k[lo:lo_next], Wk)
+            pk = feature(k[lo:lo_next], Wk)
             s = s + pk.T @ v[lo:lo_next]
             z = z + pk.sum(axis=0)
     if return_states:
@@ -262,12 +324,12 @@ def recurrent_step(state: Dict[str, object], q_c, k_c, v_c, Wq, Wk, *, HW: int, 
     kw = np.concatenate([state["k_tail"], k_c])
     vw = np.concatenate([state["v_tail"], v_c])
     ES = np.exp((q_c @ kw.T) / math.sqrt(D))
-    pq = phi(q_c, Wq)
+    pq = feature(q_c, Wq)
     y = (ES @ vw + pq @ S) / (ES.sum(axis=1) + pq @ z)[:, None]
     # Keys of the window that no later window reaches: all but the last To frames.
     n_keep = min(To * HW, kw.shape[0])
     n_fold = kw.shape[0] - n_keep
-    pk = phi(kw[:n_fold], Wk)
+    pk = feature(kw[:n_fold], Wk)
     new = {"S": S + pk.T @ vw[:n_fold], "z": z + pk.sum(axis=0),
            "k_tail": kw[n_fold:].copy(), "v_tail": vw[n_fold:].copy(),
            "t": int(state["t"]) + 1}

@@ -7,7 +7,12 @@ least one pin far off.
 
 Sources for the definitions: papernotes.org note "ReHyAt: Recurrent Hybrid Attention for
 Video Diffusion Transformers", key design 1 (chunked split, joint normalisation), key
-design 2 (overlapped softmax set), key design 4 (causal linear set, chunk-wise RNN).
+design 2 (overlapped softmax set), key design 3 (feature maps), key design 4 (causal linear
+set, chunk-wise RNN).
+
+Feature maps are passed as the Wq / Wk arguments: a D x F matrix (the fixed map
+1 + u + u^2/2) or a map object; `make_map` builds the map objects of key design 3 from a
+plain description, so the pins do not depend on how the oracle implements them.
 """
 from __future__ import annotations
 
@@ -20,6 +25,8 @@ import numpy as np
 import torch
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked_tiny.json")
+GOLDEN_MAPS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "hand_worked_feature_maps.json")
 
 Attn = Callable[..., np.ndarray]
 
@@ -172,9 +179,157 @@ def pin_brute_force(attn: Attn) -> float:
     return worst
 
 
+# ---- feature maps of key design 3 ----------------------------------------------------------
+
+class EluMap:
+    """1 + elu(x) elementwise, restated here for the pins."""
+    kind = "elu"
+
+    def __call__(self, x):
+        x = np.asarray(x, dtype=np.float64)
+        return np.where(x > 0, 1.0 + x, np.exp(np.minimum(x, 0.0)))
+
+    def dim(self, D):
+        return D
+
+
+class PolyMlpMap:
+    """relu(x W1 + b1) W2 + b2 split into P parts, part i to the power i (restated)."""
+    kind = "poly_mlp"
+
+    def __init__(self, W1, b1, W2, b2, P=2):
+        self.W1, self.b1 = np.asarray(W1, float), np.asarray(b1, float)
+        self.W2, self.b2 = np.asarray(W2, float), np.asarray(b2, float)
+        self.P = P
+
+    def __call__(self, x):
+        psi = np.maximum(np.asarray(x, float) @ self.W1 + self.b1, 0.0) @ self.W2 + self.b2
+        n = psi.shape[-1] // self.P
+        return np.concatenate([psi[..., i * n:(i + 1) * n] ** (i + 1) for i in range(self.P)],
+                              axis=-1)
+
+    def dim(self, D):
+        return self.W2.shape[1]
+
+
+def make_map(desc):
+    if desc["map"] == "elu":
+        return EluMap()
+    return PolyMlpMap(desc["W1"], desc["b1"], desc["W2"], desc["b2"], desc.get("P", 2))
+
+
+def pin_golden_feature_maps(attn: Attn) -> float:
+    """Hand-derived outputs of tests/golden/hand_worked_feature_maps.json, both modes."""
+    with open(GOLDEN_MAPS) as f:
+        cases = json.load(f)["cases"]
+    worst = 0.0
+    for c in cases:
+        q, k, v = (np.array(c[n], dtype=np.float64) for n in ("q", "k", "v"))
+        m = make_map(c)
+        for mode in ("causal", "bidir"):
+            expected = np.array([[_eval_formula(e)] for e in c[mode]])
+            y = attn(q, k, v, m, m, c["HW"], c["Tc"], c["To"], mode == "causal")
+            worst = max(worst, float(np.abs(y - expected).max()))
+    return worst
+
+
+def pin_constant_map_closed_form(attn: Attn) -> float:
+    """W2 = 0 makes the learned map constant, phi = [b2 part 1, (b2 part 2)^2]: every linear
+    pair weighs c = |phi|^2, so y = (Z_S * A_S + c * sum_L v) / (Z_S + c * |L|) with A_S
+    and Z_S from the library (SDPA, logsumexp) over each chunk's window."""
+    worst = 0.0
+    for (T, HW, Tc, To, D, h, F, seed) in ((6, 3, 2, 1, 8, 5, 4, 41), (5, 2, 1, 2, 4, 3, 6, 42)):
+        N = T * HW
+        q, k, v = (_rand((N, D), seed + i) for i in range(3))
+        b2 = _rand((F,), seed + 5)
+        m = PolyMlpMap(_rand((D, h), seed + 6), _rand((h,), seed + 7), np.zeros((h, F)), b2)
+        c = float((b2[:F // 2] ** 2).sum() + (b2[F // 2:] ** 4).sum())
+        Np = Tc * HW
+        for causal in (True, False):
+            y = attn(q, k, v, m, m, HW, Tc, To, causal)
+            ref = np.empty_like(y)
+            t = 0
+            while t * Np < N:
+                r0, r1 = t * Np, min((t + 1) * Np, N)
+                lo, hi = max(t * Np - To * HW, 0), r1
+                L = list(range(0, lo)) + ([] if causal else list(range(hi, N)))
+                A = _sdpa(q[r0:r1], k[lo:hi], v[lo:hi])
+                logits = torch.from_numpy(q[r0:r1] @ k[lo:hi].T / math.sqrt(D))
+                Z = torch.logsumexp(logits, dim=1).exp().numpy()[:, None]
+                sv = v[L].sum(axis=0) if L else np.zeros(v.shape[1])
+                ref[r0:r1] = (Z * A + c * sv) / (Z + c * len(L))
+                t += 1
+            worst = max(worst, float(np.abs(y - ref).max()))
+    return worst
+
+
+def _phi_row_loops(x, m):
+    """A map of key design 3 applied to one row with pure-Python loops."""
+    if m.kind == "elu":
+        return [1.0 + a if a > 0 else math.exp(a) for a in x]
+    W1, b1, W2, b2 = m.W1.tolist(), m.b1.tolist(), m.W2.tolist(), m.b2.tolist()
+    hid = [max(sum(x[d] * W1[d][j] for d in range(len(x))) + b1[j], 0.0) for j in range(len(b1))]
+    psi = [sum(hid[j] * W2[j][f] for j in range(len(hid))) + b2[f] for f in range(len(b2))]
+    n = len(psi) // m.P
+    return [psi[f] ** (f // n + 1) for f in range(len(psi))]
+
+
+def brute_force_maps(q, k, v, mq, mk, HW, Tc, To, causal):
+    """Like brute_force, with feature maps of key design 3 computed by loops."""
+    N, D = len(q), len(q[0])
+    Np = Tc * HW
+    y = []
+    for n in range(N):
+        t = n // Np
+        lo = max(t * Np - To * HW, 0)
+        hi = min((t + 1) * Np, N)
+        pq = _phi_row_loops(q[n], mq)
+        num = [0.0] * len(v[0])
+        den = 0.0
+        for j in range(N):
+            if lo <= j < hi:
+                w = math.exp(sum(q[n][d] * k[j][d] for d in range(D)) / math.sqrt(D))
+            elif j < lo or (not causal and j >= hi):
+                w = sum(a * b for a, b in zip(pq, _phi_row_loops(k[j], mk)))
+            else:
+                continue
+            den += w
+            for d in range(len(num)):
+                num[d] += w * v[j][d]
+        y.append([x / den for x in num])
+    return np.array(y)
+
+
+def pin_brute_force_feature_maps(attn: Attn) -> float:
+    """Oracle vs pure-Python brute force with the elu map and with learned maps (separate
+    maps for queries and keys), several (Tc, To), both modes, a ragged last chunk."""
+    worst = 0.0
+    seed = 300
+    for (T, HW, Tc, To) in ((4, 2, 1, 0), (5, 1, 2, 1), (4, 2, 3, 2), (5, 2, 2, 3)):
+        seed += 1
+        N, D, h, F = T * HW, 3, 4, 4
+        q, k, v = (_rand((N, D), seed + i) for i in range(3))
+        maps = [(EluMap(), EluMap())]
+        mq = PolyMlpMap(_rand((D, h), seed + 5, 0.7), _rand((h,), seed + 6, 0.3),
+                        _rand((h, F), seed + 7, 0.6), _rand((F,), seed + 8, 0.5) + 1.0)
+        mk = PolyMlpMap(_rand((D, h), seed + 9, 0.7), _rand((h,), seed + 10, 0.3),
+                        _rand((h, F), seed + 11, 0.6), _rand((F,), seed + 12, 0.5) + 1.0)
+        maps.append((mq, mk))
+        for (a, b) in maps:
+            for causal in (True, False):
+                y = attn(q, k, v, a, b, HW, Tc, To, causal)
+                ref = brute_force_maps(q.tolist(), k.tolist(), v.tolist(), a, b, HW, Tc, To,
+                                       causal)
+                worst = max(worst, float(np.abs(y - ref).max()))
+    return worst
+
+
 ALL_PINS = {
     "golden": pin_golden,
     "softmax_special_cases": pin_softmax_special_cases,
     "w_zero_closed_form": pin_w_zero_closed_form,
     "brute_force": pin_brute_force,
+    "golden_feature_maps": pin_golden_feature_maps,
+    "constant_map_closed_form": pin_constant_map_closed_form,
+    "brute_force_feature_maps": pin_brute_force_feature_maps,
 }

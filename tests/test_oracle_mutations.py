@@ -13,7 +13,31 @@ import pytest
 from tests import oracle_pins as pins
 
 
+def _map(x, m, bug):
+    """The feature maps of key design 3 (objects from tests/oracle_pins.py), restated."""
+    x = np.asarray(x, dtype=np.float64)
+    if isinstance(m, pins.EluMap):
+        if bug == "elu_minus_one":
+            return np.where(x > 0, x, np.exp(np.minimum(x, 0.0)) - 1.0)
+        if bug == "elu_no_exp_branch":
+            return 1.0 + x
+        return np.where(x > 0, 1.0 + x, np.exp(np.minimum(x, 0.0)))
+    pre = x @ m.W1 + (0.0 if bug == "mlp_no_bias1" else m.b1)
+    hid = pre if bug == "mlp_no_relu" else np.maximum(pre, 0.0)
+    psi = hid @ m.W2 + (0.0 if bug == "mlp_no_bias2" else m.b2)
+    if bug == "mlp_no_power":
+        return psi
+    n = psi.shape[-1] // m.P
+    parts = [psi[..., i * n:(i + 1) * n] for i in range(m.P)]
+    if bug == "mlp_power_on_first_part":
+        parts = parts[::-1]
+        return np.concatenate([p ** (i + 1) for i, p in enumerate(parts)][::-1], axis=-1)
+    return np.concatenate([p ** (i + 1) for i, p in enumerate(parts)], axis=-1)
+
+
 def _phi(x, W, bug):
+    if isinstance(W, (pins.EluMap, pins.PolyMlpMap)):
+        return _map(x, W, bug)
     D = x.shape[-1]
     if bug == "phi_transposed_w":
         u = x @ W.T / math.sqrt(D)
@@ -90,6 +114,8 @@ BUGS = [
     "linear_includes_window", "causal_mask_in_chunk", "uncompensated_max",
     "drop_softmax_after_chunk0", "drop_linear", "linear_values_from_keys",
     "linear_missing_from_denominator",
+    "elu_minus_one", "elu_no_exp_branch", "mlp_no_relu", "mlp_no_bias1", "mlp_no_bias2",
+    "mlp_no_power", "mlp_power_on_first_part",
 ]
 
 

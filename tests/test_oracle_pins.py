@@ -14,8 +14,18 @@ from tests import oracle_pins as pins
 TOL = 1e-12
 
 
+def oracle_map(m):
+    """The oracle's own map object for a pin's map description (matrices pass through)."""
+    if isinstance(m, pins.EluMap):
+        return orc.EluFeatureMap()
+    if isinstance(m, pins.PolyMlpMap):
+        return orc.PolyMlpFeatureMap(m.W1, m.b1, m.W2, m.b2, m.P)
+    return m
+
+
 def attn_oracle(q, k, v, Wq, Wk, HW, Tc, To, causal):
-    return orc.hybrid_attention(q, k, v, Wq, Wk, HW=HW, Tc=Tc, To=To, causal=causal)
+    return orc.hybrid_attention(q, k, v, oracle_map(Wq), oracle_map(Wk), HW=HW, Tc=Tc, To=To,
+                                causal=causal)
 
 
 @pytest.mark.parametrize("name", sorted(pins.ALL_PINS))
@@ -209,3 +219,40 @@ def test_rows_subset_matches_full():
     y = orc.hybrid_attention(q, k, v, W, W, HW=HW, Tc=Tc, To=To)
     ys = orc.hybrid_attention(q, k, v, W, W, HW=HW, Tc=Tc, To=To, rows=rows)
     assert np.abs(ys - y[rows]).max() < 1e-13
+
+
+def test_feature_maps_hand_values():
+    # 1 + elu(x): x + 1 above zero, exp(x) at or below it.
+    e = orc.EluFeatureMap()(np.array([[0.0, 1.0, -1.0, 2.5]]))
+    assert np.allclose(e, [[1.0, 2.0, math.exp(-1.0), 3.5]], rtol=0, atol=1e-15)
+    # learned map, D = h = 2, F = 2, P = 2: pre-activation x W1 + b1 with W1 = I, b1 = (0, -1);
+    # x = (1, 2): relu(1, 1) = (1, 1); psi = (1, 1) W2 + b2 = (1 + 0.5, 2 + 1 + 0) = (1.5, 3);
+    # phi = (1.5, 3^2) = (1.5, 9). x = (-1, 0.5): relu(-1, -0.5) = 0, psi = b2 = (0.5, 0).
+    m = orc.PolyMlpFeatureMap(np.eye(2), [0.0, -1.0], [[1.0, 2.0], [0.0, 1.0]], [0.5, 0.0], P=2)
+    assert np.array_equal(m(np.array([[1.0, 2.0], [-1.0, 0.5]])), np.array([[1.5, 9.0], [0.5, 0.0]]))
+    # P = 1 is the plain 2-layer network; P = 2 with F = 4 squares the last two outputs.
+    m1 = orc.PolyMlpFeatureMap(np.eye(2), [0.0, -1.0], [[1.0, 2.0], [0.0, 1.0]], [0.5, 0.0], P=1)
+    assert np.array_equal(m1(np.array([[1.0, 2.0]])), np.array([[1.5, 3.0]]))
+    m4 = orc.PolyMlpFeatureMap([[1.0]], [0.0], [[1.0, -1.0, 2.0, -3.0]], [0.0, 0.0, 0.0, 0.0], P=2)
+    assert np.array_equal(m4(np.array([[2.0]])), np.array([[2.0, -2.0, 16.0, 36.0]]))
+    assert orc.feature_dim(m4, 1) == 4 and orc.feature_dim(orc.EluFeatureMap(), 7) == 7
+
+
+def test_feature_map_recurrence_and_state():
+    """The chunk-wise RNN and the direct state sums agree with the pairwise definition for
+    the maps of key design 3 (separate query and key maps)."""
+    rng = np.random.default_rng(9)
+    T, HW, Tc, To, D, h, F = 7, 3, 2, 1, 8, 6, 4
+    N = T * HW
+    q, k, v = (rng.standard_normal((N, D)) for _ in range(3))
+    mq = orc.PolyMlpFeatureMap(rng.standard_normal((D, h)) / 3, rng.standard_normal(h) * 0.2,
+                               rng.standard_normal((h, F)) / 2, rng.standard_normal(F) * 0.3 + 1)
+    mk = orc.PolyMlpFeatureMap(rng.standard_normal((D, h)) / 3, rng.standard_normal(h) * 0.2,
+                               rng.standard_normal((h, F)) / 2, rng.standard_normal(F) * 0.3 + 1)
+    for (a, b) in ((orc.EluFeatureMap(), orc.EluFeatureMap()), (mq, mk)):
+        y = orc.hybrid_attention(q, k, v, a, b, HW=HW, Tc=Tc, To=To, causal=True)
+        yr, states = orc.hybrid_recurrent(q, k, v, a, b, HW=HW, Tc=Tc, To=To, return_states=True)
+        assert np.abs(y - yr).max() < 1e-12
+        for t, (lo_t) in enumerate(l[2] for l in orc.chunk_layout(T, HW, Tc, To)):
+            S, z = orc.state_direct(k, v, b, lo_t)
+            assert np.abs(states[t][0] - S).max() < 1e-12 and np.abs(states[t][1] - z).max() < 1e-12
