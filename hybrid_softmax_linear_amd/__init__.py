@@ -22,10 +22,12 @@ __all__ = [
     "rehyat_hybrid_fwd", "rehyat_hybrid_fwd_workspace",
     "rehyat_recurrent_step", "rehyat_recurrent_step_workspace",
     "rehyat_timing_enable", "rehyat_timing_read", "F32", "BF16", "CAUSAL", "BIDIR",
+    "PHI_POLY2", "PHI_ELU", "PHI_MLP",
 ]
 
 F32, BF16 = 0, 1
 CAUSAL, BIDIR = 0, 1
+PHI_POLY2, PHI_ELU, PHI_MLP = 0, 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "librehyat.so")
@@ -43,7 +45,7 @@ class RehyatError(RuntimeError):
 class _CDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "H", "T", "HW", "D", "F", "Tc", "To", "dtype", "y_dtype", "mode",
-                 "w_per_head")]
+                 "w_per_head", "phi_kind", "phi_hidden", "phi_parts")]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -61,6 +63,9 @@ class Desc:
     y_dtype: int = F32
     mode: int = CAUSAL
     w_per_head: int = 0
+    phi_kind: int = PHI_POLY2
+    phi_hidden: int = 0
+    phi_parts: int = 0
 
     @property
     def N(self) -> int:
@@ -145,7 +150,7 @@ def _stream(stream) -> Optional[int]:
 
 
 def rehyat_phi(desc: Desc, x, n: int, W, phi, stream=None) -> None:
-    """phi [B,H,n,F] = 1 + u + u^2/2, u = x W / sqrt(D) (see include/rehyat.h)."""
+    """phi [B,H,n,F] of the feature map desc.phi_kind names (see include/rehyat.h)."""
     _check(lib().rehyat_phi(ctypes.byref(desc.c()), _ptr(x), int(n), _ptr(W), _ptr(phi),
                             _stream(stream)), "rehyat_phi")
 

@@ -36,6 +36,10 @@ hipError_t launch_copy_rows(const void* sk, const void* sv, void* dk, void* dv, 
 hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH,
                                      int F, void* img, int64_t img_bh, int64_t img_t,
                                      const void* W, int nW, void* wimg, hipStream_t stream);
+hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* params,
+                               int per_head, int H, int hid, int P, int BH, int F, void* out,
+                               hipStream_t stream);
+hipError_t launch_state_partial_phi_bf16(const StateArgs& a, int F, int BH, hipStream_t stream);
 }  // namespace rehyat
 
 using namespace rehyat;
@@ -92,6 +96,19 @@ rehyat_status check_desc(const rehyat_desc* d) {
     if (d->F % 16 != 0 || d->F > 256)
       return fail(REHYAT_ERR_UNSUPPORTED, "fp32 path supports F = 16..256, multiple of 16 (got %d)", d->F);
   }
+  if (d->phi_kind != REHYAT_PHI_POLY2 && d->phi_kind != REHYAT_PHI_ELU &&
+      d->phi_kind != REHYAT_PHI_MLP)
+    return fail(REHYAT_ERR_DTYPE, "phi_kind %d unknown", d->phi_kind);
+  if (d->phi_kind != REHYAT_PHI_POLY2 && d->dtype != REHYAT_BF16)
+    return fail(REHYAT_ERR_UNSUPPORTED, "phi_kind %d needs dtype bf16", d->phi_kind);
+  if (d->phi_kind == REHYAT_PHI_ELU && d->F != d->D)
+    return fail(REHYAT_ERR_SHAPE, "1 + elu needs F = D (got F = %d, D = %d)", d->F, d->D);
+  if (d->phi_kind == REHYAT_PHI_MLP) {
+    if (d->phi_hidden != 64 && d->phi_hidden != 128 && d->phi_hidden != 256)
+      return fail(REHYAT_ERR_UNSUPPORTED, "phi_hidden must be 64, 128 or 256 (got %d)", d->phi_hidden);
+    if (d->phi_parts < 1 || d->F % d->phi_parts != 0)
+      return fail(REHYAT_ERR_SHAPE, "F = %d does not split into phi_parts = %d parts", d->F, d->phi_parts);
+  }
   const int64_t N = (int64_t)d->T * d->HW;
   const int64_t BH = (int64_t)d->B * d->H;
   const int64_t width = d->D > d->F ? d->D : d->F;
@@ -101,6 +118,32 @@ rehyat_status check_desc(const rehyat_desc* d) {
 }
 
 int n_chunks(const rehyat_desc* d) { return (d->T + d->Tc - 1) / d->Tc; }
+
+// Feature maps of kind 1 and 2 are evaluated ahead into bf16 phi rows.
+bool phi_ahead(const rehyat_desc* d) { return d->phi_kind != REHYAT_PHI_POLY2; }
+bool needs_w(const rehyat_desc* d) { return d->phi_kind != REHYAT_PHI_ELU; }
+
+// Bytes of one W argument (all heads).
+size_t w_bytes(const rehyat_desc* d) {
+  const size_t heads = d->w_per_head ? d->H : 1;
+  if (d->phi_kind == REHYAT_PHI_ELU) return 0;
+  if (d->phi_kind == REHYAT_PHI_MLP) {
+    const size_t h = d->phi_hidden;
+    return heads * ((size_t)d->D * h + h + h * d->F + d->F) * 2;
+  }
+  return heads * d->D * d->F * (d->dtype == REHYAT_BF16 ? 2 : 4);
+}
+
+// bf16 phi rows of n rows per head.
+size_t phi_rows_bytes(const rehyat_desc* d, int64_t n) {
+  return (size_t)d->B * d->H * (size_t)n * d->F * 2;
+}
+
+hipError_t launch_phi_rows(const rehyat_desc* d, const void* x, int64_t n, const void* W,
+                           void* out, hipStream_t s) {
+  return launch_phi_map_bf16(d->phi_kind, x, n, W, d->w_per_head, d->H, d->phi_hidden,
+                             d->phi_parts, d->B * d->H, d->F, out, s);
+}
 
 size_t state_elems(const rehyat_desc* d) { return (size_t)d->F * d->D + d->F; }
 
@@ -141,6 +184,7 @@ hipError_t launch_attention(const rehyat_desc* d, AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_partial(const rehyat_desc* d, const StateArgs& sa, hipStream_t s) {
   const int BH = d->B * d->H;
+  if (sa.phik) return launch_state_partial_phi_bf16(sa, d->F, BH, s);
   return (d->dtype == REHYAT_BF16) ? launch_state_partial_bf16(sa, d->F, BH, s)
                                    : launch_state_partial_f32(sa, d->D, d->F, BH, s);
 }
@@ -181,7 +225,7 @@ size_t fwd_vt_bytes(const rehyat_desc* d) {
 // F*256 bytes per state (S^T) and per W (W^T).
 size_t image_bytes(const rehyat_desc* d) { return (size_t)d->F * 256; }
 size_t w_images_bytes(const rehyat_desc* d) {
-  if (d->dtype != REHYAT_BF16) return 0;
+  if (d->dtype != REHYAT_BF16 || phi_ahead(d)) return 0;
   return (size_t)(d->w_per_head ? d->H : 1) * image_bytes(d);
 }
 
@@ -220,16 +264,17 @@ rehyat_status rehyat_phi(const rehyat_desc* d, const void* x, int64_t n, const v
   if (st != REHYAT_OK) return st;
   if (n < 0) return fail(REHYAT_ERR_SHAPE, "n < 0");
   if (n == 0) return ok();
-  if (!x || !W || !phi) return fail(REHYAT_ERR_NULL, "x, W and phi must be non-NULL");
+  if (!x || (needs_w(d) && !W) || !phi) return fail(REHYAT_ERR_NULL, "x, W and phi must be non-NULL");
   if (!aligned16(x) || !aligned16(W) || !aligned16(phi))
     return fail(REHYAT_ERR_ALIGN, "x, W, phi must be 16-byte aligned");
   const int64_t BH = (int64_t)d->B * d->H;
   if (BH * n * (d->D > d->F ? d->D : d->F) >= kMaxElems) return fail(REHYAT_ERR_SHAPE, "n too large");
   const size_t es = esize(d->dtype);
   if (overlaps(phi, BH * n * d->F * es, x, BH * n * d->D * es) ||
-      overlaps(phi, BH * n * d->F * es, W, (size_t)(d->w_per_head ? d->H : 1) * d->D * d->F * es))
+      overlaps(phi, BH * n * d->F * es, W, w_bytes(d)))
     return fail(REHYAT_ERR_ALIAS, "phi overlaps an input");
   hipStream_t s = (hipStream_t)stream;
+  if (phi_ahead(d)) return hip_status(launch_phi_rows(d, x, n, W, phi, s), "rehyat_phi launch");
   const float us = 1.0f / std::sqrt((float)d->D);
   hipError_t e = (d->dtype == REHYAT_BF16)
                      ? launch_phi_bf16(x, n, W, d->w_per_head, d->H, (int)BH, d->F, phi, 0, us, s)
@@ -240,7 +285,9 @@ rehyat_status rehyat_phi(const rehyat_desc* d, const void* x, int64_t n, const v
 size_t rehyat_state_update_workspace(const rehyat_desc* d, int64_t n) {
   if (check_desc(d) != REHYAT_OK || n <= 0) return 0;
   const int64_t nseg = (n + kStateSegRows - 1) / kStateSegRows;
-  return (size_t)d->B * d->H * nseg * state_elems(d) * sizeof(float);
+  // per-segment partial states, then (maps evaluated ahead) the phi(k) rows
+  return (size_t)d->B * d->H * nseg * state_elems(d) * sizeof(float) +
+         (phi_ahead(d) ? phi_rows_bytes(d, n) : 0);
 }
 
 rehyat_status rehyat_state_update(const rehyat_desc* d, const void* k, const void* v, int64_t n,
@@ -250,7 +297,8 @@ rehyat_status rehyat_state_update(const rehyat_desc* d, const void* k, const voi
   if (st != REHYAT_OK) return st;
   if (n < 0) return fail(REHYAT_ERR_SHAPE, "n < 0");
   if (n == 0) return ok();
-  if (!k || !v || !Wk || !S || !z) return fail(REHYAT_ERR_NULL, "k, v, Wk, S, z must be non-NULL");
+  if (!k || !v || (needs_w(d) && !Wk) || !S || !z)
+    return fail(REHYAT_ERR_NULL, "k, v, Wk, S, z must be non-NULL");
   if (!aligned16(k) || !aligned16(v) || !aligned16(Wk) || !aligned16(S) || !aligned16(z))
     return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
   const int64_t BH = (int64_t)d->B * d->H;
@@ -275,6 +323,12 @@ rehyat_status rehyat_state_update(const rehyat_desc* d, const void* k, const voi
   sa.part = reinterpret_cast<float*>(ws);
   sa.u_scale = 1.0f / std::sqrt((float)d->D);
   hipStream_t s = (hipStream_t)stream;
+  if (phi_ahead(d)) {
+    void* phik = reinterpret_cast<unsigned char*>(ws) + (size_t)BH * sa.n_seg * state_elems(d) * 4;
+    hipError_t e = launch_phi_rows(d, k, n, Wk, phik, s);
+    if (e != hipSuccess) return hip_status(e, "phi launch");
+    sa.phik = phik; sa.phik_rows = n;
+  }
   hipError_t e = launch_partial(d, sa, s);
   if (e != hipSuccess) return hip_status(e, "state partial launch");
   e = launch_fold_states(sa.part, sa.n_seg, S, z, d->F, d->D, 0, (int)BH, s);
@@ -286,8 +340,11 @@ size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* d) {
   const size_t BH = (size_t)d->B * d->H;
   const size_t imgs = (d->dtype == REHYAT_BF16 && n_chunks(d) > 1)
                           ? BH * n_chunks(d) * image_bytes(d) + w_images_bytes(d) : 0;
+  // maps evaluated ahead: phi(k) and phi(q) rows of the whole sequence
+  const size_t phis = (phi_ahead(d) && n_chunks(d) > 1)
+                          ? 2 * phi_rows_bytes(d, (int64_t)d->T * d->HW) : 0;
   return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + fwd_vt_bytes(d) +
-         imgs;
+         imgs + phis;
 }
 
 rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
@@ -295,7 +352,8 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
                                 void* stream) {
   rehyat_status st = check_desc(d);
   if (st != REHYAT_OK) return st;
-  if (!q || !k || !v || !Wq || !Wk || !y) return fail(REHYAT_ERR_NULL, "q, k, v, Wq, Wk, y must be non-NULL");
+  if (!q || !k || !v || (needs_w(d) && (!Wq || !Wk)) || !y)
+    return fail(REHYAT_ERR_NULL, "q, k, v, Wq, Wk, y must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(Wq) || !aligned16(Wk) ||
       !aligned16(y))
     return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
@@ -306,7 +364,7 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   const int BH = d->B * d->H;
   const size_t es = esize(d->dtype);
   const size_t nin = (size_t)BH * N * d->D * es, ny = (size_t)BH * N * d->D * esize(d->y_dtype);
-  const size_t nw = (size_t)(d->w_per_head ? d->H : 1) * d->D * d->F * es;
+  const size_t nw = w_bytes(d);
   if (overlaps(y, ny, q, nin) || overlaps(y, ny, k, nin) || overlaps(y, ny, v, nin) ||
       overlaps(y, ny, Wq, nw) || overlaps(y, ny, Wk, nw) || overlaps(ws, need, y, ny) ||
       overlaps(ws, need, q, nin) || overlaps(ws, need, k, nin) || overlaps(ws, need, v, nin))
@@ -320,6 +378,8 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   void* vt = states + (size_t)BH * nch * E;                  // V^T (bf16 path)
   unsigned char* simg = reinterpret_cast<unsigned char*>(vt) + fwd_vt_bytes(d);   // S^T images
   unsigned char* wimg = simg + (size_t)BH * nch * image_bytes(d);                 // W^T images
+  unsigned char* phik = wimg + w_images_bytes(d);            // phi rows (maps evaluated ahead)
+  unsigned char* phiq = phik + phi_rows_bytes(d, N);
   const float us = 1.0f / std::sqrt((float)d->D);
   const bool need_state = nch > 1;   // a single chunk has an empty linear set in both modes
   const bool bf16 = d->dtype == REHYAT_BF16;
@@ -337,6 +397,12 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
     sa.u_scale = us;
     sa.vt_out = fused_vt ? vt : nullptr;
     sa.vt_ld = N;
+    if (phi_ahead(d)) {
+      hipError_t e = launch_phi_rows(d, k, N, Wk, phik, s);
+      if (e == hipSuccess) e = launch_phi_rows(d, q, N, Wq, phiq, s);
+      if (e != hipSuccess) return hip_status(e, "phi launch");
+      sa.phik = phik; sa.phik_rows = N;
+    }
     hipError_t e = launch_partial(d, sa, s);
     if (e != hipSuccess) return hip_status(e, "state partial launch");
     e = launch_scan_states(part, states, d->F, d->D, d->T, d->Tc, d->To, nch,
@@ -345,7 +411,7 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
     if (bf16) {
       e = launch_linear_images_bf16(states, (int64_t)nch * E, (int64_t)E, nch, BH, d->F, simg,
                                     (int64_t)(nch * image_bytes(d)), (int64_t)image_bytes(d), Wq,
-                                    d->w_per_head ? d->H : 1, wimg, s);
+                                    d->w_per_head ? d->H : 1, phi_ahead(d) ? nullptr : wimg, s);
       if (e != hipSuccess) return hip_status(e, "linear image launch");
     }
   }
@@ -372,6 +438,7 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   a.s_bh = (int64_t)nch * E; a.s_t = (int64_t)E; a.z_bh = a.s_bh; a.z_t = a.s_t;
   a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
   a.st_img = simg; a.st_img_bh = (int64_t)(nch * image_bytes(d)); a.st_img_t = (int64_t)image_bytes(d);
+  a.phiq = (phi_ahead(d) && need_state) ? phiq : nullptr;
   a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
   a.n_chunks = nch; a.chunk0 = 0; a.step = 0;
   a.bidir = d->mode == REHYAT_BIDIR;
@@ -387,8 +454,12 @@ size_t rehyat_recurrent_step_workspace(const rehyat_desc* d) {
   if (check_desc(d) != REHYAT_OK) return 0;
   const size_t imgs = (d->dtype == REHYAT_BF16)
                           ? (size_t)d->B * d->H * image_bytes(d) + w_images_bytes(d) : 0;
+  // maps evaluated ahead: phi(q) of the chunk and phi(k) of the gathered window
+  const size_t phis = phi_ahead(d) ? phi_rows_bytes(d, (int64_t)d->Tc * d->HW) +
+                                         phi_rows_bytes(d, step_nk_max(d))
+                                   : 0;
   return (size_t)d->B * d->H * d->Tc * state_elems(d) * sizeof(float) + step_gather_bytes(d) +
-         imgs;
+         imgs + phis;
 }
 
 rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void* q_c,
@@ -402,7 +473,7 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
   if (t < 0 || t >= nch) return fail(REHYAT_ERR_SHAPE, "chunk_index %d outside [0, %d)", t, nch);
   const int cf = (d->T - t * d->Tc) < d->Tc ? (d->T - t * d->Tc) : d->Tc;   // frames in chunk
   if (cf < d->To) return fail(REHYAT_ERR_UNSUPPORTED, "final chunk of %d frames is shorter than To = %d", cf, d->To);
-  if (!q_c || !k_c || !v_c || !Wq || !Wk || !S || !z || !y_c)
+  if (!q_c || !k_c || !v_c || (needs_w(d) && (!Wq || !Wk)) || !S || !z || !y_c)
     return fail(REHYAT_ERR_NULL, "q_c, k_c, v_c, Wq, Wk, S, z, y_c must be non-NULL");
   if (d->To > 0 && (!k_tail || !v_tail)) return fail(REHYAT_ERR_NULL, "k_tail, v_tail needed when To > 0");
   if (!aligned16(q_c) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(Wq) || !aligned16(Wk) ||
@@ -441,6 +512,9 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
   a.ka = k_tail ? k_tail : k_c; a.va = v_tail ? v_tail : v_c; a.a_rows = k_tail ? trow : crow;
   a.kb = k_c; a.vb = v_c; a.b_rows = crow;
   float* part = reinterpret_cast<float*>(ws);
+  void* phiq_step = nullptr;   // phi(q_c) rows (maps evaluated ahead)
+  void* phik_step = nullptr;   // phi rows of the gathered window keys
+  void* kwin_step = nullptr;
   if (d->dtype == REHYAT_BF16) {
     // gather the window contiguously: K [nk_max][D] and V^T [D][ld] per head
     uint16_t* kwin = reinterpret_cast<uint16_t*>(part + (size_t)BH * d->Tc * state_elems(d));
@@ -450,11 +524,19 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
     unsigned char* simg = reinterpret_cast<unsigned char*>(part + (size_t)BH * d->Tc * state_elems(d)) +
                           step_gather_bytes(d);
     unsigned char* wimg = simg + (size_t)BH * image_bytes(d);
+    phiq_step = wimg + w_images_bytes(d);
+    phik_step = reinterpret_cast<unsigned char*>(phiq_step) + phi_rows_bytes(d, (int64_t)d->Tc * d->HW);
     if (t > 0) {
       hipError_t ei = launch_linear_images_bf16(S, (int64_t)d->F * d->D, 0, 1, BH, d->F, simg,
                                                 (int64_t)image_bytes(d), 0, Wq,
-                                                d->w_per_head ? d->H : 1, wimg, s);
+                                                d->w_per_head ? d->H : 1,
+                                                phi_ahead(d) ? nullptr : wimg, s);
       if (ei != hipSuccess) return hip_status(ei, "linear image launch");
+      if (phi_ahead(d)) {
+        ei = launch_phi_rows(d, q_c, crow, Wq, phiq_step, s);
+        if (ei != hipSuccess) return hip_status(ei, "phi launch");
+        a.phiq = phiq_step;
+      }
     }
     a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
     a.st_img = simg; a.st_img_bh = (int64_t)image_bytes(d); a.st_img_t = 0;
@@ -463,6 +545,7 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
                                              kwin, step_nk_max(d), BH, s);
     if (e != hipSuccess) return hip_status(e, "window gather launch");
     a.ka = kwin; a.a_rows = step_nk_max(d);
+    kwin_step = kwin;
     a.vt = vtwin; a.vt_bh = (int64_t)d->D * ld; a.vt_t = 0; a.vt_ld = ld; a.vt_key0_is_lo = 0;
   }
   a.Wq = Wq; a.w_per_head = d->w_per_head;
@@ -490,6 +573,13 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
     sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
     sa.part = part;
     sa.u_scale = us;
+    if (phi_ahead(d)) {
+      // phi of the gathered window keys (tail rows, then chunk rows: the fold's row order;
+      // all nk_max rows of each head's window buffer, of which the first nfold are used)
+      e = launch_phi_rows(d, kwin_step, step_nk_max(d), Wk, phik_step, s);
+      if (e != hipSuccess) return hip_status(e, "phi launch");
+      sa.phik = phik_step; sa.phik_rows = step_nk_max(d);
+    }
     e = launch_partial(d, sa, s);
     if (e != hipSuccess) return hip_status(e, "state partial launch");
     e = launch_fold_states(part, sa.n_seg, S, z, d->F, d->D, t == 0, BH, s);

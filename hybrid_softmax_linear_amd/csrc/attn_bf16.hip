@@ -193,7 +193,7 @@ __device__ __forceinline__ void pv_mfma(Acc& A, const bf16x8 (&vf)[4][2], const 
 template <int F>
 __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs& a,
                                               const Geo& g, const QRegs& Q, unsigned char* stage,
-                                              float* zs, int tid, int lane) {
+                                              float* zs, int tid, int lane, const uint16_t* pqrow) {
   const int wave = tid >> 6;
   const float* z = a.z + g.bh * a.z_bh + g.t_local * a.z_t;
   float nl = 0.0f;
@@ -220,8 +220,9 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
     for (int i = 0; i < (SLAB / 1024 + NW - 1) / NW; ++i) {
       const int j = wave + NW * i;
       if (j < SLAB / 1024) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wt + j * 1024), 16,
-                                                 base + j * 1024 + lane * 16, 0, 0, 0);
+        if (!a.phiq)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wt + j * 1024), 16,
+                                                   base + j * 1024 + lane * 16, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(st + j * 1024), 16,
                                                  base + j * 1024 + lane * 16, 0, 0, 0);
       }
@@ -233,6 +234,22 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
     constexpr int G = F > 128 ? 2 : NFB;
 #pragma unroll
     for (int fg = 0; fg < NFB; fg += G) {
+      bf16x8 P[G][2];
+      if (a.phiq) {
+        // phi(q) computed ahead: this lane's 8 consecutive features per operand
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int fbase = f0 + 32 * (fg + k) + 16 * j + 8 * (lane >> 5);
+            const u32x4 w4 = pqrow ? *reinterpret_cast<const u32x4*>(pqrow + fbase)
+                                   : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              nl += bf16_lo(w4[e]) * zs[fbase + 2 * e] + bf16_hi(w4[e]) * zs[fbase + 2 * e + 1];
+            P[k][j] = as_bf16x8(w4);
+          }
+      } else {
       f32x16 U[G];
 #pragma unroll
       for (int k = 0; k < G; ++k)
@@ -247,7 +264,6 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
           U[k] = mfma32(av, Q.op[s], U[k]);
         }
       // phi = 1 + u + u^2/2, rounded to bf16: B operand of a^L^T = S^T phi^T.
-      bf16x8 P[G][2];
 #pragma unroll
       for (int k = 0; k < G; ++k)
 #pragma unroll
@@ -266,6 +282,7 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
           }
           P[k][j] = as_bf16x8(pk);
         }
+      }
 #pragma unroll
       for (int k = 0; k < G; ++k)
 #pragma unroll
@@ -293,15 +310,18 @@ __device__ __forceinline__ void zero_acc(Acc& A) {
 }
 
 // With O = a^L (from linear_branch) and reference m0: O = a^L/n^L * w, l = w (in one lane
-// of the pair), w = 2^(log2 n^L - m0), the weight of the linear "key".
+// of the pair), w = n^L 2^(-m0) computed as sign(n^L) 2^(log2 |n^L| - m0), the weight of the
+// linear "key". (Learned feature maps can make n^L zero or negative: the scale then stays
+// 2^(-m0) and the sign is kept; for n^L > 0 this is exactly w = 2^(log2 n^L - m0).)
 __device__ __forceinline__ void scale_linear(Acc& A, float nl, float m0, int lane) {
-  const float w = fast_exp2(fast_log2(nl) - m0);
-  const float sc = w / nl;
+  const float an = fabsf(nl);
+  const float w = fast_exp2(fast_log2(an) - m0);
+  const float sc = an > 0.0f ? w / an : fast_exp2(-m0);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) A.O[db][i] *= sc;
-  A.l = (lane < 32) ? w : 0.0f;
+  A.l = (lane < 32) ? __builtin_copysignf(w, nl) : 0.0f;
 }
 
 // One 128-key tile from LDS: four 32-key blocks of S^T = K Q^T, p = 2^(s*ls - m0),
@@ -533,9 +553,14 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   Acc A;
   float nl = 1.0f, ml = kNegBig;
   zero_acc(A);
+  const uint16_t* pqrow =
+      (a.phiq && active && qrow < g.rows)
+          ? reinterpret_cast<const uint16_t*>(a.phiq) +
+                ((int64_t)g.bh * a.q_rows + g.q_row_base + qrow) * F
+          : nullptr;
   if (g.has_linear) {
-    linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane);
-    ml = fast_log2(nl);
+    linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane, pqrow);
+    ml = fast_log2(fabsf(nl));
   }
   float m0 = start_window(ml, src, Q, smem, ls, wave, lane);
   if (g.has_linear) scale_linear(A, nl, m0, lane);
@@ -554,7 +579,7 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
       const float mx = max_sweep(src, Q, smem, ls, wave, lane);
       zero_acc(A);
       tile_dma(src, 0, smem, wave, lane);
-      if (g.has_linear) linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane);
+      if (g.has_linear) linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane, pqrow);
       // reference = the exact maximum over the linear weight and every window key: every
       // p <= 1 and l >= 1
       m0 = start_window(fmaxf(ml, mx), src, Q, smem, ls, wave, lane);

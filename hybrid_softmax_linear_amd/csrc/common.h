@@ -137,6 +137,9 @@ struct AttnArgs {
   // (bh, t) at st_img + bh*st_img_bh + t*st_img_t bytes) in the LDS slab layout
   const void* wt_img; int64_t wt_img_head;
   const void* st_img; int64_t st_img_bh, st_img_t;
+  // bf16 path, feature maps computed ahead (learned / elu maps): phi(q) rows [.][q_rows][F]
+  // with the same row indexing as q; NULL: phi(q) = 1 + u + u^2/2 computed in the kernel
+  const void* phiq;
   int H;
   int HW, Tc, To, T;    // geometry of the whole video
   int n_chunks;         // chunks handled by this launch
@@ -164,6 +167,9 @@ struct StateArgs {
   float u_scale;
   // optional (bf16 path): V^T of the virtual rows, [BH][D][vt_ld] bf16, column = row index
   void* vt_out; int64_t vt_ld;
+  // optional (bf16 path): phi(k) computed ahead, virtual row w of head bh at
+  // phik + (bh * phik_rows + w) * F; NULL: phi(k) = 1 + u + u^2/2 from Wk in the kernel
+  const void* phik; int64_t phik_rows;
 };
 
 }  // namespace rehyat

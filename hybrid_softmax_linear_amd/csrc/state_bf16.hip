@@ -329,6 +329,298 @@ wt_image_kernel(const uint16_t* __restrict__ W, int F, unsigned char* __restrict
   }
 }
 
+// Per-segment partial states from phi(k) rows computed ahead (feature maps other than
+// 1 + u + u^2/2): the phi rows of a 64-row tile are staged row-major (rows of 2F + 64
+// bytes) and enter dS = phi(K)^T V as the A operand through transposing LDS reads; V is
+// staged transposed as in state_partial_bf16_kernel. dz = sum of phi over the tile's rows.
+template <int F>
+__global__ void __launch_bounds__(256)
+state_partial_phi_bf16_kernel(StateArgs a) {
+  constexpr int PLD = F * 2 + 64;
+  constexpr int PPR = F / 8;                         // 16-byte pieces per phi row
+  constexpr int PIT = kTileRows * PPR / 256;         // phi pieces per thread and tile
+  __shared__ __attribute__((aligned(16))) unsigned char pt[kTileRows * PLD];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[kVTileBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = blockIdx.x % a.n_seg;
+  const int bh = blockIdx.x / a.n_seg;
+  const int64_t r0 = (int64_t)seg * a.seg_len;
+  const int64_t r1 = (r0 + a.seg_len < a.n) ? r0 + a.seg_len : a.n;
+  const int nrows = (int)(r1 - r0);
+  const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.phik) + ((int64_t)bh * a.phik_rows + r0) * F;
+
+  RowSrc vs;
+  {
+    const uint16_t* va = reinterpret_cast<const uint16_t*>(a.va) + head_off(bh, a.a_rows, kDim);
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.vb) + head_off(bh, a.b_rows, kDim);
+    const int64_t na_rel = (a.na - r0) > 0 ? (a.na - r0) : 0;
+    vs = RowSrc{va, vb + (r0 > a.na ? (r0 - a.na) * kDim : 0) + a.b_row0 * kDim,
+                a.a_row0 + r0, na_rel, (int64_t)nrows};
+  }
+
+  constexpr int PW = FBlocks<F>::per_wave;
+  const bool active = wave < FBlocks<F>::total;
+  f32x16 acc[PW][4];
+  float zp[PW];
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    zp[p] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[p][db][i] = 0.0f;
+  }
+
+  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
+  u32x4 pr[PIT], vr[4];
+  auto load = [&](int64_t w0) {
+#pragma unroll
+    for (int it = 0; it < PIT; ++it) {
+      const int id = it * 256 + tid, row = id / PPR, c = id - row * PPR;
+      pr[it] = (w0 + row < nrows) ? *reinterpret_cast<const u32x4*>(ph + (w0 + row) * F + 8 * c)
+                                  : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int id = it * 256 + tid, row = id >> 4, c = id & 15;
+      vr[it] = (w0 + row < nrows) ? *reinterpret_cast<const u32x4*>(row_ptr(vs, w0 + row) + c * 8)
+                                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load(0);
+#pragma unroll 1
+  for (int ti = 0; ti < ntiles; ++ti) {
+    __syncthreads();   // previous tile fully consumed
+#pragma unroll
+    for (int it = 0; it < PIT; ++it) {
+      const int id = it * 256 + tid, row = id / PPR, c = id - row * PPR;
+      *reinterpret_cast<u32x4*>(pt + row * PLD + c * 16) = pr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int id = it * 256 + tid, row = id >> 4, c = id & 15;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned w = vr[it][e >> 1];
+        *reinterpret_cast<uint16_t*>(vt + vtile_off(c * 8 + e, row)) =
+            (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+      }
+    }
+    if (ti + 1 < ntiles) load((int64_t)(ti + 1) * kTileRows);
+    __syncthreads();
+    if (a.vt_out) {
+      uint16_t* vo = reinterpret_cast<uint16_t*>(a.vt_out) + (int64_t)bh * kDim * a.vt_ld +
+                     r0 + ti * kTileRows;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int id = it * 256 + tid;
+        const int d = id >> 3, kc = id & 7;
+        if (ti * kTileRows + 8 * kc < nrows)
+          *reinterpret_cast<u32x4*>(vo + (int64_t)d * a.vt_ld + 8 * kc) =
+              *reinterpret_cast<const u32x4*>(vt + vtile_chunk_off(d, kc));
+      }
+    }
+    if (!active) continue;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (ti * kTileRows + kb * 32 >= nrows) break;
+#pragma unroll
+      for (int p = 0; p < PW; ++p) {
+        const int fb = wave + 4 * p;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 af = frag_tr(pt, PLD, 32 * kb + 16 * j, 32 * fb, lane);
+          const u32x4 au = as_u32x4(af);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zp[p] += bf16_lo(au[e]) + bf16_hi(au[e]);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int d = 32 * db + (lane & 31);
+            const bf16x8 bv = as_bf16x8(lds_read16(vt, vtile_chunk_off(d, 4 * kb + 2 * j + (lane >> 5))));
+            acc[p][db] = mfma32(af, bv, acc[p][db]);
+          }
+        }
+      }
+    }
+  }
+
+  if (!active) return;
+  const int E = F * kDim + F;
+  float* out = a.part + ((int64_t)bh * a.n_seg + seg) * E;
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    const int fb = wave + 4 * p;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int f = 32 * fb + crow(i, lane);
+        out[(int64_t)f * kDim + d] = acc[p][db][i];
+      }
+    }
+    const float zf = pair_sum(zp[p]);
+    if (lane < 32) out[F * kDim + 32 * fb + lane] = zf;
+  }
+}
+
+// ---- feature maps of key design 3, materialised as bf16 rows ------------------------------
+//
+// 1 + elu(x) (F = D): elementwise.
+// Learned polynomial map: psi = relu(x W1 + b1) W2 + b2 (W1 [D][h], W2 [h][F]), split into P
+// equal parts, part i (1-based) raised to the power i. Computed transposed, lane = row:
+// H^T = W1^T X^T and Psi^T = W2^T H^T on bf16 MFMA (fp32 accumulation); with the A rows
+// taken in kappa order, the accumulator of H^T (bias, ReLU, rounded to bf16) is directly the
+// B operand of the second product. phi is rounded to bf16 on store.
+
+__global__ void __launch_bounds__(256)
+phi_elu_bf16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ out, int64_t units) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8 elements per unit
+  if (i >= units) return;
+  const u32x4 v = reinterpret_cast<const u32x4*>(x)[i];
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = bf16_lo(v[e]), b = bf16_hi(v[e]);
+    w[e] = pack_bf16_u32(a > 0.0f ? 1.0f + a : __expf(a), b > 0.0f ? 1.0f + b : __expf(b));
+  }
+  reinterpret_cast<u32x4*>(out)[i] = w;
+}
+
+// Transposing stage of rows [0, nrows) x columns [c0, c0+ncols) of src (row length ld, bf16)
+// into dst rows = columns (ncols rows of nrows bf16, row bytes 2*nrows), 16-byte chunk c of a
+// row at chunk c ^ (row & mask). 256 threads.
+__device__ __forceinline__ void stage_t(unsigned char* dst, const uint16_t* src, int ld, int c0,
+                                        int nrows, int ncols, int mask, int tid) {
+  const int cpr = ncols / 8;                 // 8-column pieces per source row
+  for (int id = tid; id < nrows * cpr; id += 256) {
+    const int r = id / cpr, c = id - r * cpr;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + (int64_t)r * ld + c0 + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * c + e;              // destination row = source column
+      const uint16_t hv = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(dst + row * (nrows * 2) + ((((r >> 3) ^ (row & mask))) << 4) +
+                                   ((r & 7) << 1)) = hv;
+    }
+  }
+}
+
+constexpr int kMlpRowTiles = 4;   // 128-row tiles per workgroup
+
+template <int F, int HID>
+__global__ void __launch_bounds__(256)
+phi_mlp_bf16_kernel(const uint16_t* __restrict__ x, int64_t n, const uint16_t* __restrict__ params,
+                    int64_t head_elems, int H, int P, uint16_t* __restrict__ out,
+                    int blocks_per_head) {
+  constexpr int FS = F < 128 ? F : 128;
+  constexpr int hid = HID;
+  __shared__ __attribute__((aligned(16))) unsigned char w1t[HID * 256];   // [h][128]
+  __shared__ __attribute__((aligned(16))) unsigned char w2t[FS * HID * 2]; // [FS][h]
+  __shared__ float b1s[HID], b2s[F];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.x / blocks_per_head;
+  const int blk = blockIdx.x - bh * blocks_per_head;
+  const uint16_t* p = params + (head_elems ? (int64_t)(bh % H) * head_elems : 0);
+  const uint16_t* W1 = p;
+  const uint16_t* b1 = W1 + (int64_t)kDim * hid;
+  const uint16_t* W2 = b1 + hid;
+  const uint16_t* b2 = W2 + (int64_t)hid * F;
+  const uint16_t* xh = x + (int64_t)bh * n * kDim;
+  uint16_t* oh = out + (int64_t)bh * n * F;
+  constexpr int hmask = (HID / 8 < 16 ? HID / 8 : 16) - 1;
+  // W1^T: rows j (hidden), d chunk at chunk ^ (j & 15) over 16 chunks of 128 d
+  stage_t(w1t, W1, hid, 0, kDim, hid, 15, tid);
+  for (int j = tid; j < hid; j += 256) b1s[j] = bf16_to_f32(((const bf16*)b1)[j]);
+  for (int f = tid; f < F; f += 256) b2s[f] = bf16_to_f32(((const bf16*)b2)[f]);
+  const int part = F / P;
+#pragma unroll 1
+  for (int f0 = 0; f0 < F; f0 += FS) {
+    __syncthreads();
+    stage_t(w2t, W2, F, f0, hid, FS, hmask, tid);   // W2^T slab: rows f, hidden chunks
+    __syncthreads();
+#pragma unroll 1
+    for (int rt = 0; rt < kMlpRowTiles; ++rt) {
+      const int64_t row = ((int64_t)blk * kMlpRowTiles + rt) * 128 + wave * 32 + (lane & 31);
+      const bool ok = row < n;
+      bf16x8 xop[8];
+      {
+        const uint16_t* src = xh + (ok ? row : 0) * kDim + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          xop[s] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(src + 16 * s) : u32x4{0u, 0u, 0u, 0u});
+      }
+      // Hidden block jb (32 units): H^T block, bias, ReLU, bf16; its two 16-unit k-steps go
+      // straight into every output tile of the slab.
+      f32x16 Ps[FS / 32];
+#pragma unroll
+      for (int fb = 0; fb < FS / 32; ++fb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Ps[fb][i] = 0.0f;
+#pragma unroll 1
+      for (int jb = 0; jb < HID / 32; ++jb) {
+        f32x16 Hc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Hc[i] = 0.0f;
+        const int arow = 32 * jb + kappa(lane & 31);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const int c = 2 * s2 + (lane >> 5);
+          Hc = mfma32(as_bf16x8(lds_read16(w1t, arow * 256 + ((c ^ (arow & 15)) << 4))), xop[s2], Hc);
+        }
+        bf16x8 hb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i0 = 8 * j + 2 * e;
+            const int u = 32 * jb + cidx(i0, lane);
+            pk[e] = pack_bf16_u32(fmaxf(Hc[i0] + b1s[u], 0.0f), fmaxf(Hc[i0 + 1] + b1s[u + 1], 0.0f));
+          }
+          hb[j] = as_bf16x8(pk);
+        }
+#pragma unroll
+        for (int fb = 0; fb < FS / 32; ++fb) {
+          const int frow = 32 * fb + kappa(lane & 31);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int c = 2 * (2 * jb + j) + (lane >> 5);
+            Ps[fb] = mfma32(as_bf16x8(lds_read16(w2t, frow * (HID * 2) + ((c ^ (frow & hmask)) << 4))),
+                            hb[j], Ps[fb]);
+          }
+        }
+      }
+      // phi of the slab's features: bias, part powers, bf16 rows
+#pragma unroll
+      for (int fb = 0; fb < FS / 32; ++fb) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int fbase = f0 + 32 * fb + 16 * j + 8 * (lane >> 5);
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v2[2];
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+              const int i = 8 * j + 2 * e + q2;
+              const int f = fbase + 2 * e + q2;
+              const float psi = Ps[fb][i] + b2s[f];
+              const int pw = f / part + 1;
+              float v = psi;
+              for (int k2 = 1; k2 < pw; ++k2) v *= psi;
+              v2[q2] = v;
+            }
+            pk[e] = pack_bf16_u32(v2[0], v2[1]);
+          }
+          if (ok) *reinterpret_cast<u32x4*>(oh + row * F + fbase) = pk;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather_window_bf16(const void* ka, const void* va, int64_t a_rows, int64_t a_row0,
@@ -388,6 +680,52 @@ hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, 
     dim3 grid(F / 32, nW), block(256);
     hipLaunchKernelGGL(wt_image_kernel, grid, block, 0, stream, (const uint16_t*)W, F,
                        (unsigned char*)wimg);
+  }
+  return hipGetLastError();
+}
+
+// phi rows of a feature map of key design 3 into out [BH][n][F] bf16. kind 1: 1 + elu(x)
+// (F = D, params unused); kind 2: the learned polynomial map with the parameter blocks
+// [W1 D*hid][b1 hid][W2 hid*F][b2 F] (bf16) at params (+ (bh % H) * block if per head).
+hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* params,
+                               int per_head, int H, int hid, int P, int BH, int F, void* out,
+                               hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (kind == 1) {
+    const int64_t units = (int64_t)BH * n * kDim / 8;
+    dim3 grid((unsigned)((units + 255) / 256)), block(256);
+    hipLaunchKernelGGL(phi_elu_bf16_kernel, grid, block, 0, stream, (const uint16_t*)x,
+                       (uint16_t*)out, units);
+    return hipGetLastError();
+  }
+  if (kind != 2 || P < 1 || F % P) return hipErrorInvalidValue;
+  const int64_t head_elems = per_head ? (int64_t)kDim * hid + hid + (int64_t)hid * F + F : 0;
+  const int bph = (int)((n + 128 * kMlpRowTiles - 1) / (128 * kMlpRowTiles));
+  dim3 grid(BH * bph), block(256);
+  const uint16_t* xx = (const uint16_t*)x;
+  const uint16_t* pp = (const uint16_t*)params;
+  uint16_t* oo = (uint16_t*)out;
+#define REHYAT_MLP(FF, HH)                                                                    \
+  if (F == FF && hid == HH) {                                                                 \
+    hipLaunchKernelGGL((phi_mlp_bf16_kernel<FF, HH>), grid, block, 0, stream, xx, n, pp,        \
+                       head_elems, H, P, oo, bph);                                            \
+    return hipGetLastError();                                                                 \
+  }
+  REHYAT_MLP(64, 64) REHYAT_MLP(64, 128) REHYAT_MLP(64, 256)
+  REHYAT_MLP(128, 64) REHYAT_MLP(128, 128) REHYAT_MLP(128, 256)
+  REHYAT_MLP(256, 64) REHYAT_MLP(256, 128) REHYAT_MLP(256, 256)
+#undef REHYAT_MLP
+  return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_state_partial_phi_bf16(const StateArgs& a, int F, int BH, hipStream_t stream) {
+  dim3 grid(BH * a.n_seg), block(256);
+  switch (F) {
+    case 64:  hipLaunchKernelGGL(state_partial_phi_bf16_kernel<64>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(state_partial_phi_bf16_kernel<128>, grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(state_partial_phi_bf16_kernel<256>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -87,6 +87,27 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, unsigned char* kt,
   }
 }
 
+// Transposing fragment read (ds_read_b64_tr_b16) from a row-major bf16 tile with row
+// stride `ld` bytes: lane l receives the 8 consecutive rows row0 + 8 (l/32) .. +7 of column
+// col0 + (l mod 32), the operand layout of a 32x32x16 MFMA whose contraction runs over
+// those rows. Within each 16-lane group lane r addresses row row0 + 8 (group/2) + r/4 at
+// columns col0 + 16 (group mod 2) + 4 (r mod 4) .. +3, and lane j of the group receives
+// the four rows of column col0 + 16 (group mod 2) + j. With ld = 16 words mod 64 words the
+// four rows one 32-lane pass reads sit on disjoint banks.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int ld, int row0, int col0,
+                                          int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const int row = row0 + 8 * (g >> 1) + (r >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (r & 3);
+  const unsigned char* p = tile + row * ld + col * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Stage W^T for features [f0, f0+nf) into LDS as [nf][128 d] rows of 256 B, in the K-tile
 // layout (row f, chunk c at c ^ kappa(f & 15)). W is [128 d][F] bf16 (row-major).
 __device__ __forceinline__ void stage_wt(unsigned char* dst, const uint16_t* W, int F, int f0,

@@ -5,13 +5,15 @@ points; no arithmetic happens here.
 """
 from __future__ import annotations
 
+import dataclasses
 from typing import Optional
 
 import torch
 
-from . import (BF16, BIDIR, CAUSAL, F32, Desc, rehyat_hybrid_fwd, rehyat_hybrid_fwd_workspace,
-               rehyat_phi, rehyat_recurrent_step, rehyat_recurrent_step_workspace,
-               rehyat_state_update, rehyat_state_update_workspace)
+from . import (BF16, BIDIR, CAUSAL, F32, PHI_ELU, PHI_MLP, PHI_POLY2, Desc, rehyat_hybrid_fwd,
+               rehyat_hybrid_fwd_workspace, rehyat_phi, rehyat_recurrent_step,
+               rehyat_recurrent_step_workspace, rehyat_state_update,
+               rehyat_state_update_workspace)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -22,12 +24,51 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def make_desc(q: torch.Tensor, W: torch.Tensor, *, T: int, HW: int, Tc: int, To: int,
-              causal: bool = True, y_dtype: torch.dtype = torch.float32) -> Desc:
+@dataclasses.dataclass(frozen=True)
+class FeatureMap:
+    """Which feature map phi the library evaluates (rehyat_desc.phi_kind and its sizes).
+    The fixed map (the default) takes F from its W [D, F] / [H, D, F]."""
+    kind: int = PHI_POLY2
+    F: int = 0
+    hidden: int = 0
+    parts: int = 0
+
+
+def elu_map(D: int = 128) -> FeatureMap:
+    """phi = 1 + elu(x), F = D; it takes no parameters (pass W = None)."""
+    return FeatureMap(PHI_ELU, F=D)
+
+
+def mlp_map(F: int, hidden: int, parts: int = 2) -> FeatureMap:
+    """The learned polynomial map; its W is a parameter block from mlp_param_block."""
+    return FeatureMap(PHI_MLP, F=F, hidden=hidden, parts=parts)
+
+
+def mlp_param_block(W1, b1, W2, b2) -> torch.Tensor:
+    """Concatenate W1 [D, h], b1 [h], W2 [h, F], b2 [F] (or the same with a leading head
+    dimension) into the bf16 parameter block the library reads ([n] or [H, n])."""
+    per_head = W1.dim() == 3
+    lead = (W1.shape[0],) if per_head else ()
+    parts = [t.reshape(lead + (-1,)) for t in (W1, b1, W2, b2)]
+    return torch.cat(parts, dim=-1).to(torch.bfloat16).contiguous()
+
+
+def _map_fields(W: Optional[torch.Tensor], fmap: Optional[FeatureMap]):
+    """(F, w_per_head, phi_kind, phi_hidden, phi_parts) of a W argument."""
+    if fmap is None or fmap.kind == PHI_POLY2:
+        return W.shape[-1], 1 if W.dim() == 3 else 0, PHI_POLY2, 0, 0
+    per_head = 1 if (fmap.kind == PHI_MLP and W is not None and W.dim() == 2) else 0
+    return fmap.F, per_head, fmap.kind, fmap.hidden, fmap.parts
+
+
+def make_desc(q: torch.Tensor, W: Optional[torch.Tensor], *, T: int, HW: int, Tc: int, To: int,
+              causal: bool = True, y_dtype: torch.dtype = torch.float32,
+              fmap: Optional[FeatureMap] = None) -> Desc:
     B, H, _, D = q.shape
-    return Desc(B=B, H=H, T=T, HW=HW, D=D, F=W.shape[-1], Tc=Tc, To=To, dtype=_dtype_code(q),
-                y_dtype=_DT[y_dtype], mode=CAUSAL if causal else BIDIR,
-                w_per_head=1 if W.dim() == 3 else 0)
+    F, wph, kind, hid, parts = _map_fields(W, fmap)
+    return Desc(B=B, H=H, T=T, HW=HW, D=D, F=F, Tc=Tc, To=To, dtype=_dtype_code(q),
+                y_dtype=_DT[y_dtype], mode=CAUSAL if causal else BIDIR, w_per_head=wph,
+                phi_kind=kind, phi_hidden=hid, phi_parts=parts)
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -36,13 +77,15 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def hybrid_fwd(q, k, v, Wq, Wk=None, *, HW: int, Tc: int, To: int, causal: bool = True,
                y_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
-               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+               ws: Optional[torch.Tensor] = None,
+               fmap: Optional[FeatureMap] = None) -> torch.Tensor:
     """Whole-sequence hybrid attention of q, k, v [B, H, N, D] (N a multiple of HW)."""
     Wk = Wq if Wk is None else Wk
     N = q.shape[2]
     if N % HW:
         raise ValueError("N must be a multiple of HW")
-    d = make_desc(q, Wq, T=N // HW, HW=HW, Tc=Tc, To=To, causal=causal, y_dtype=y_dtype)
+    d = make_desc(q, Wq, T=N // HW, HW=HW, Tc=Tc, To=To, causal=causal, y_dtype=y_dtype,
+                  fmap=fmap)
     y = torch.empty(q.shape, dtype=y_dtype, device=q.device) if out is None else out
     if ws is None:
         ws = workspace(rehyat_hybrid_fwd_workspace(d), q.device)
@@ -50,20 +93,18 @@ def hybrid_fwd(q, k, v, Wq, Wk=None, *, HW: int, Tc: int, To: int, causal: bool 
     return y
 
 
-def phi(x, W) -> torch.Tensor:
+def phi(x, W, fmap: Optional[FeatureMap] = None) -> torch.Tensor:
     B, H, n, D = x.shape
-    d = Desc(B=B, H=H, T=1, HW=1, D=D, F=W.shape[-1], Tc=1, To=0, dtype=_dtype_code(x),
-             w_per_head=1 if W.dim() == 3 else 0)
-    out = torch.empty((B, H, n, W.shape[-1]), dtype=x.dtype, device=x.device)
+    d = make_desc(x, W, T=1, HW=1, Tc=1, To=0, fmap=fmap)
+    out = torch.empty((B, H, n, d.F), dtype=x.dtype, device=x.device)
     rehyat_phi(d, x, n, W, out)
     return out
 
 
-def state_update(k, v, Wk, S, z) -> None:
+def state_update(k, v, Wk, S, z, fmap: Optional[FeatureMap] = None) -> None:
     """S += sum phi(k) v^T, z += sum phi(k) (in place)."""
-    B, H, n, D = k.shape
-    d = Desc(B=B, H=H, T=1, HW=1, D=D, F=Wk.shape[-1], Tc=1, To=0, dtype=_dtype_code(k),
-             w_per_head=1 if Wk.dim() == 3 else 0)
+    n = k.shape[2]
+    d = make_desc(k, Wk, T=1, HW=1, Tc=1, To=0, fmap=fmap)
     ws = workspace(rehyat_state_update_workspace(d, n), k.device)
     rehyat_state_update(d, k, v, n, Wk, S, z, ws)
 
@@ -74,9 +115,11 @@ class Recurrent:
 
     def __init__(self, B: int, H: int, D: int, F: int, *, T: int, HW: int, Tc: int, To: int,
                  dtype: torch.dtype = torch.bfloat16, y_dtype: torch.dtype = torch.float32,
-                 w_per_head: bool = False, device="cuda"):
+                 w_per_head: bool = False, device="cuda", fmap: Optional[FeatureMap] = None):
+        fm = fmap or FeatureMap()
         self.desc = Desc(B=B, H=H, T=T, HW=HW, D=D, F=F, Tc=Tc, To=To, dtype=_DT[dtype],
-                         y_dtype=_DT[y_dtype], mode=CAUSAL, w_per_head=int(w_per_head))
+                         y_dtype=_DT[y_dtype], mode=CAUSAL, w_per_head=int(w_per_head),
+                         phi_kind=fm.kind, phi_hidden=fm.hidden, phi_parts=fm.parts)
         self.S = torch.zeros((B, H, F, D), dtype=torch.float32, device=device)
         self.z = torch.zeros((B, H, F), dtype=torch.float32, device=device)
         rows = max(To * HW, 1)

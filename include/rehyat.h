@@ -14,7 +14,21 @@
  *     a^L = phi(q) (sum_L phi(k) v^T), n^S, n^L the matching weight sums (key design 1).
  *     No stabiliser enters the result: running maxima inside the kernels are compensated
  *     exactly.
- *   - Feature map: phi(x)_i = 1 + u_i + u_i^2/2, u = x W / sqrt(D), W a D x F matrix.
+ *   - Feature map phi, chosen by desc->phi_kind (key design 3):
+ *       REHYAT_PHI_POLY2 (0): phi(x)_i = 1 + u_i + u_i^2/2, u = x W / sqrt(D); W is a D x F
+ *         matrix ([D, F], or [H, D, F] with w_per_head).
+ *       REHYAT_PHI_ELU (1): phi(x) = 1 + elu(x) elementwise (x + 1 for x > 0, exp(x)
+ *         otherwise), the linear-attention baseline the note compares with. F = D; W is
+ *         unused and may be NULL.
+ *       REHYAT_PHI_MLP (2): the learned polynomial map: psi = relu(x W1 + b1) W2 + b2 (one
+ *         hidden layer of h = phi_hidden units), split into P = phi_parts equal parts of
+ *         F/P features, part i (i = 1..P) raised elementwise to the power i. W points to the
+ *         parameter block, bf16, row-major, concatenated: W1 [D, h], b1 [h], W2 [h, F],
+ *         b2 [F] (D*h + h + h*F + F elements); with w_per_head, H such blocks back to back.
+ *         The note fixes neither the activation nor P: ReLU and the block layout are this
+ *         library's choice, P is a parameter (the plainest reading is P = 2).
+ *       Maps 1 and 2 can give phi(q).phi(k) of either sign; n^L then enters the joint
+ *       normalisation with its sign.
  *   - Causal form as a chunk-wise RNN (key design 4): state S = sum phi(k) v^T (F x D) and
  *     z = sum phi(k) (F) over the keys already out of reach of the softmax window.
  *
@@ -33,7 +47,10 @@
  *   - Outputs must not overlap inputs.
  *   - Supported sizes: bf16: D = 128, F in {64, 128, 256}. fp32: D in {64, 128},
  *     F in {16, 32, ..., 256} (a multiple of 16). B, H >= 1; T, HW, Tc >= 1; To >= 0;
- *     B*H*T*HW*max(D,F) < 2^31 elements per tensor.
+ *     B*H*T*HW*max(D,F) < 2^31 elements per tensor. phi_kind 1 and 2 need dtype bf16;
+ *     phi_kind 2 needs phi_hidden in {64, 128, 256} and F a multiple of phi_parts >= 1.
+ *   - phi_kind 1 and 2 evaluate phi(q) and phi(k) into the workspace ahead of the attention
+ *     and state kernels (bf16 rows); their *_workspace() sizes include those rows.
  */
 #ifndef REHYAT_H
 #define REHYAT_H
@@ -59,6 +76,7 @@ typedef enum {
 
 typedef enum { REHYAT_F32 = 0, REHYAT_BF16 = 1 } rehyat_dtype;
 typedef enum { REHYAT_CAUSAL = 0, REHYAT_BIDIR = 1 } rehyat_mode;
+typedef enum { REHYAT_PHI_POLY2 = 0, REHYAT_PHI_ELU = 1, REHYAT_PHI_MLP = 2 } rehyat_phi_kind;
 
 /* Problem description shared by all entry points. */
 typedef struct {
@@ -69,14 +87,16 @@ typedef struct {
   int32_t dtype;      /* rehyat_dtype of q, k, v, W, k_tail, v_tail */
   int32_t y_dtype;    /* rehyat_dtype of y */
   int32_t mode;       /* rehyat_mode (rehyat_hybrid_fwd only; the step path is causal) */
-  int32_t w_per_head; /* 0: Wq and Wk are [D, F] shared by all heads; 1: they are [H, D, F] */
+  int32_t w_per_head; /* 0: Wq and Wk are shared by all heads; 1: one per head (H of them) */
+  int32_t phi_kind;   /* rehyat_phi_kind of the feature map (0: the fixed polynomial) */
+  int32_t phi_hidden; /* REHYAT_PHI_MLP: hidden units h; ignored otherwise */
+  int32_t phi_parts;  /* REHYAT_PHI_MLP: number of parts P; ignored otherwise */
 } rehyat_desc;
 
 /*
- * Feature map phi (the fixed polynomial map above; the ReHyAt note's key design 3 uses a
- * learned polynomial map in its place).
+ * Feature map phi of key design 3, of the kind desc->phi_kind names (see above).
  *   x   [B, H, n, D]  dtype     (device)
- *   W   [D, F] or [H, D, F]     (device)
+ *   W   the map's parameters, as described above for each phi_kind (device)
  *   phi [B, H, n, F]  dtype     (device, written)
  * n >= 0 rows per (b, h); n = 0 is a no-op.
  */
@@ -87,7 +107,7 @@ rehyat_status rehyat_phi(const rehyat_desc* desc, const void* x, int64_t n, cons
  * Recurrent-state update (key design 4, the sums s and z of the chunk-wise RNN):
  *   S[b,h] += sum_{rows r} phi(k_r) v_r^T,   z[b,h] += sum_r phi(k_r)
  *   k, v  [B, H, n, D]  dtype   (device)
- *   Wk    [D, F] or [H, D, F]   (device)
+ *   Wk    parameters of phi (see phi_kind above) (device)
  *   S     [B, H, F, D]  fp32    (device, read and written)
  *   z     [B, H, F]     fp32    (device, read and written)
  *   ws    device scratch of at least rehyat_state_update_workspace(desc, n) bytes.
@@ -103,7 +123,8 @@ rehyat_status rehyat_state_update(const rehyat_desc* desc, const void* k, const 
  * the non-recursive form of the chunk-wise RNN) or bidirectional (REHYAT_BIDIR).
  *   q, k, v [B, H, N, D] dtype  (device), N = T*HW; T need not be a multiple of Tc (the
  *                                last chunk is then shorter)
- *   Wq, Wk  [D, F] or [H, D, F] (device; may be the same buffer)
+ *   Wq, Wk  parameters of the maps applied to q and to k (see phi_kind above; device; may
+ *           be the same buffer)
  *   y       [B, H, N, D] y_dtype (device, written)
  *   ws      device scratch of at least rehyat_hybrid_fwd_workspace(desc) bytes (per-frame
  *           partial states and the per-chunk linear-branch states).

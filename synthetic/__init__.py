@@ -20,6 +20,16 @@ Recipe: one torch.Generator (CPU) seeded with the config's seed; draws in this o
   3. q, k, v [B, H, N, D] ~ N(0, 1), float32, in that order.
 Then every tensor is rounded to the storage dtype (bf16 with round-to-nearest-even, or kept
 float32). torch's CPU generator gives the same draws for any thread count.
+
+Parameters of the learned polynomial feature map (make_mlp_map_params), from a generator of
+their own seed; per head when `heads` is given (leading dimension H), drawn in this order:
+  W1 [D, h] ~ N(0, 1/D)              (so x W1 ~ N(0, 1) for x ~ N(0, I_D))
+  b1 [h]    ~ N(0, b1_std^2)
+  W2 [h, F] ~ N(0, 2 psi_std^2 / h)  (relu of a unit normal has second moment 1/2, so the
+                                      random part of psi has standard deviation ~ psi_std)
+  b2 [F]    = psi_mean[i] on the features of part i (no draw)
+all rounded to bf16. psi_mean sets where psi sits; the feature products phi(q).phi(k) then
+have a known sign and scale, as a trained map imitating exp would give.
 """
 from __future__ import annotations
 
@@ -31,6 +41,7 @@ import torch
 
 __all__ = [
     "HybridConfig", "CONFIGS", "config", "make_inputs", "make_custom", "to_f64", "TORCH_DTYPE",
+    "make_mlp_map_params",
 ]
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -131,6 +142,27 @@ def make_custom(B: int, H: int, N: int, D: int, F: int, *, seed: int, dtype: str
     if scale is not None:
         out["head_scale"] = scale
     return out
+
+
+def make_mlp_map_params(D: int, hidden: int, F: int, *, seed: int, P: int = 2,
+                        heads: Optional[int] = None, psi_mean=None, psi_std: float = 0.05,
+                        b1_std: float = 0.1) -> Dict[str, torch.Tensor]:
+    """W1, b1, W2, b2 (bf16, CPU) of the learned feature map, recipe in the module
+    docstring. psi_mean: one value per part (default: 1/sqrt(F/P) on part 1, 0 elsewhere)."""
+    if F % P:
+        raise ValueError("F must split into P parts")
+    if psi_mean is None:
+        psi_mean = [1.0 / np.sqrt(F // P)] + [0.0] * (P - 1)
+    if len(psi_mean) != P:
+        raise ValueError("psi_mean needs one value per part")
+    g = torch.Generator().manual_seed(int(seed))
+    lead = () if heads is None else (int(heads),)
+    W1 = torch.randn(lead + (D, hidden), generator=g) / np.sqrt(D)
+    b1 = torch.randn(lead + (hidden,), generator=g) * b1_std
+    W2 = torch.randn(lead + (hidden, F), generator=g) * (psi_std * np.sqrt(2.0 / hidden))
+    b2 = torch.tensor(np.repeat(np.asarray(psi_mean, dtype=np.float64), F // P),
+                      dtype=torch.float32).expand(lead + (F,)).clone()
+    return {n: t.to(torch.bfloat16) for n, t in (("W1", W1), ("b1", b1), ("W2", W2), ("b2", b2))}
 
 
 def make_inputs(cfg: HybridConfig) -> Dict[str, torch.Tensor]:

@@ -155,3 +155,48 @@ def test_python_binding_raises():
     with pytest.raises(hs.RehyatError) as e:
         hs.rehyat_hybrid_fwd(d, P[0], P[1], P[2], P[3], P[4], P[5], None, 0, stream=0)
     assert e.value.name == "REHYAT_ERR_WORKSPACE"
+
+
+def test_feature_map_kind_validation():
+    assert fwd(_desc(phi_kind=3)) == ERR_DTYPE
+    assert fwd(_desc(phi_kind=hs.PHI_ELU, dtype=hs.F32)) == ERR_UNSUP    # bf16 only
+    assert fwd(_desc(phi_kind=hs.PHI_ELU, F=64)) == ERR_SHAPE            # 1 + elu: F = D
+    assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=96, phi_parts=2)) == ERR_UNSUP
+    assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=0)) == ERR_SHAPE
+    assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=3)) == ERR_SHAPE  # 128 % 3
+    # the fixed map and the learned map need W; 1 + elu has no parameters
+    assert fwd(_desc(), Wq=None) == ERR_NULL
+    assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=64, phi_parts=2), Wk=None) == ERR_NULL
+    # W = NULL passes the pointer checks for 1 + elu (each call then fails a later check)
+    L = hs.lib()
+    de = _desc(phi_kind=hs.PHI_ELU)
+    assert L.rehyat_phi(ctypes.byref(de.c()), P[0] + 2, 10, None, P[2], None) == ERR_ALIGN
+    assert fwd(de, Wq=None, Wk=None, ws=None) == ERR_WS
+    assert step(de, Wq=None, Wk=None, ws_bytes=0) == ERR_WS
+    # the learned map's parameter block [W1 D*h][b1 h][W2 h*F][b2 F] (bf16) is alias-checked
+    dm = _desc(phi_kind=hs.PHI_MLP, phi_hidden=64, phi_parts=2)
+    block = (128 * 64 + 64 + 64 * 128 + 128) * 2
+    assert L.rehyat_phi(ctypes.byref(dm.c()), P[0], 10, P[3], P[3] + block - 16, None) == ERR_ALIAS
+    assert fwd(dm, y=P[3] + block - 16) == ERR_ALIAS
+
+
+def test_feature_map_workspace_sizes():
+    L = hs.lib()
+    base = _desc()
+    BH = base.B * base.H
+    E = base.F * base.D + base.F
+    N = base.T * base.HW
+    img = base.F * 256
+    vt = BH * base.n_chunks * base.D * 64 * 2
+    gather = BH * 40 * base.D * 2 + BH * base.D * 64 * 2
+    for kw in (dict(phi_kind=hs.PHI_ELU), dict(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=2)):
+        d = _desc(**kw)
+        rows = BH * d.F * 2                      # bytes of one bf16 phi row for every head
+        # whole sequence: S^T images but no W^T image, phi(k) and phi(q) of all N rows
+        assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == (
+            BH * (d.T + d.n_chunks) * E * 4 + vt + BH * d.n_chunks * img + 2 * N * rows)
+        # one chunk: phi(q_c) of Tc*HW rows and phi of the (Tc + To)*HW window keys
+        assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == (
+            BH * d.Tc * E * 4 + gather + BH * img + (30 + 40) * rows)
+        assert L.rehyat_state_update_workspace(ctypes.byref(d.c()), 1000) == (
+            BH * 2 * E * 4 + 1000 * rows)
