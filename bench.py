@@ -12,11 +12,13 @@ read-out, windowed softmax and joint normalisation fused). Inputs are resident i
 Printed JSON line: tokens/s (value), ms per step, TFLOP/s and fraction of the bf16 MFMA
 peak over the whole step, the roofline of the dominant kernel (the attention kernel,
 timed with HIP events recorded by the library on its launch stream), the float64 CPU
-oracle timed on a bounded sample (cpu_baseline), and context timings: the same step as 7
-recurrent steps, the bidirectional form, and full softmax attention of the same shape
-(one chunk covering the whole sequence) with librehyat and with torch's SDPA.
+oracle timed on a bounded sample (cpu_baseline), and context timings: the same step with
+the learned polynomial feature map and with 1 + elu, as 7 recurrent steps, the
+bidirectional form, and full softmax attention of the same shape (one chunk covering the
+whole sequence) with librehyat and with torch's SDPA.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-context]
+    python bench.py --phi mlp|elu   the same line with another feature map of key design 3
     python bench.py --sweep     (Tc, To) grid of the ablation, one JSON line per entry
 """
 from __future__ import annotations
@@ -57,14 +59,16 @@ MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 flop/clk x 2
 HBM_PEAK_GBS = 8000.0
 
 
-def flop_model(B, H, T, HW, D, F, Tc, To, causal=True):
+def flop_model(B, H, T, HW, D, F, Tc, To, causal=True, phi_row_flop=None):
     """Algorithmic FLOPs (only what the method needs: no padding, no masked pairs).
 
-    window pairs: 4*D each (q.k and p*v); phi(q), phi(k): 2*D*F per row each; linear
+    window pairs: 4*D each (q.k and p*v); phi(q), phi(k): phi_row_flop per row each (the
+    fixed map's u = x W: 2*D*F; the learned map: 2*D*h + 2*h*F; 1 + elu: 0); linear
     read-out phi(q) S: 2*F*D per query row with a non-empty linear set; state phi(k)^T v:
     2*F*D per key that enters some linear set.
     Returns (total, attention-kernel part, state-kernel part, window pairs per head).
     """
+    pf = 2 * D * F if phi_row_flop is None else phi_row_flop
     N, Np = T * HW, Tc * HW
     pairs = rows_lin = 0
     t = 0
@@ -77,8 +81,8 @@ def flop_model(B, H, T, HW, D, F, Tc, To, causal=True):
         t += 1
     last_lo = max((t - 1) * Np - To * HW, 0)
     keys_state = N if not causal else last_lo
-    attn = 4 * D * pairs + 2 * D * F * rows_lin + 2 * F * D * rows_lin
-    state = 2 * D * F * keys_state + 2 * F * D * keys_state
+    attn = 4 * D * pairs + pf * rows_lin + 2 * F * D * rows_lin
+    state = pf * keys_state + 2 * F * D * keys_state
     BH = B * H
     return BH * (attn + state), BH * attn, BH * state, pairs
 
@@ -185,6 +189,29 @@ def sweep(args):
     return 0
 
 
+MLP_HIDDEN = 128   # hidden units of the learned feature map in the timed configurations
+
+
+def feature_map_setup(kind, cfg, dev):
+    """(Desc fields, Wq, Wk, phi FLOPs per row, label) of a feature map: "poly2" (the fixed
+    map with the workload's W), "elu" (1 + elu) or "mlp" (the learned polynomial map with
+    MLP_HIDDEN hidden units, P = 2, seeded parameters)."""
+    import synthetic as syn
+    import hybrid_softmax_linear_amd as hs
+    from hybrid_softmax_linear_amd import torch_api as ta
+    if kind == "elu":
+        return dict(F=cfg.D, phi_kind=hs.PHI_ELU), None, None, 0, "1 + elu (F = D)"
+    if kind == "mlp":
+        h = MLP_HIDDEN
+        pq = syn.make_mlp_map_params(cfg.D, h, cfg.F, seed=cfg.seed + 101)
+        pk = syn.make_mlp_map_params(cfg.D, h, cfg.F, seed=cfg.seed + 102)
+        bq = ta.mlp_param_block(pq["W1"], pq["b1"], pq["W2"], pq["b2"]).to(dev)
+        bk = ta.mlp_param_block(pk["W1"], pk["b1"], pk["W2"], pk["b2"]).to(dev)
+        return (dict(F=cfg.F, phi_kind=hs.PHI_MLP, phi_hidden=h, phi_parts=2), bq, bk,
+                2 * cfg.D * h + 2 * h * cfg.F, f"learned polynomial map (h {h}, P 2)")
+    return dict(F=cfg.F), None, None, 2 * cfg.D * cfg.F, "fixed map 1 + u + u^2/2"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +223,8 @@ def main(argv=None):
                     help="instead of the default line: time every (Tc, To) of the pages' "
                          "ablation grid at the 21x30x52 and 21x20x30 latents next to full "
                          "softmax, one JSON line per configuration")
+    ap.add_argument("--phi", choices=("poly2", "elu", "mlp"), default="poly2",
+                    help="feature map of the timed step (default: the fixed map)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (reference kernel for "
                          "the FETCH_SIZE / WRITE_SIZE counter scale)")
@@ -228,14 +257,18 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     q, k, v, W = (inp[n].to(dev) for n in ("q", "k", "v", "W"))
-    desc = hs.Desc(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, F=cfg.F, Tc=cfg.Tc, To=cfg.To,
-                   dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL)
+    base = dict(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, Tc=cfg.Tc, To=cfg.To,
+                dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL)
+    fields, Wq, Wk, phi_flop, phi_label = feature_map_setup(args.phi, cfg, dev)
+    Wq = W if Wq is None and args.phi == "poly2" else Wq
+    Wk = W if Wk is None and args.phi == "poly2" else Wk
+    desc = hs.Desc(**base, **fields)
     ws = ta.workspace(hs.rehyat_hybrid_fwd_workspace(desc), dev)
     y = torch.empty(q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
 
     def step():
-        hs.rehyat_hybrid_fwd(desc, q, k, v, W, W, y, ws, stream=stream)
+        hs.rehyat_hybrid_fwd(desc, q, k, v, Wq, Wk, y, ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -247,7 +280,8 @@ def main(argv=None):
     kern_avg = kern_ms / max(launches, 1)
 
     total_flop, attn_flop, state_flop, pairs = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D,
-                                                          cfg.F, cfg.Tc, cfg.To, causal=True)
+                                                          desc.F, cfg.Tc, cfg.To, causal=True,
+                                                          phi_row_flop=phi_flop)
     tokens = cfg.B * cfg.N
     tflops = total_flop / (ms * 1e-3) / 1e12
     attn_tflops = attn_flop / (kern_avg * 1e-3) / 1e12
@@ -255,7 +289,23 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     context = {}
-    if not args.no_context:
+    if not args.no_context and args.phi == "poly2":
+        # the other feature maps of key design 3, same workload
+        for kind in ("mlp", "elu"):
+            f2, wq2, wk2, pf2, _ = feature_map_setup(kind, cfg, dev)
+            d2 = hs.Desc(**base, **f2)
+            ws2 = ta.workspace(hs.rehyat_hybrid_fwd_workspace(d2), dev)
+            ms2 = time_calls(lambda: hs.rehyat_hybrid_fwd(d2, q, k, v, wq2, wk2, y, ws2,
+                                                           stream=stream),
+                             max(3, args.steps // 2), 2)
+            fl2 = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D, d2.F, cfg.Tc, cfg.To,
+                             causal=True, phi_row_flop=pf2)[0]
+            name = "learned_map" if kind == "mlp" else "elu_map"
+            context[f"{name}_ms"] = ms2
+            context[f"{name}_tokens_per_s"] = tokens / (ms2 * 1e-3)
+            context[f"{name}_tflops"] = fl2 / (ms2 * 1e-3) / 1e12
+            del ws2, wq2, wk2
+    if not args.no_context and args.phi == "poly2":
         # the same causal computation as 7 recurrent steps (chunks resident, contiguous)
         Np = cfg.Tc * cfg.HW
         chunks = [tuple(x[:, :, t * Np:(t + 1) * Np].contiguous() for x in (q, k, v))
@@ -314,8 +364,9 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "21x30x52 latent (480x832, 5 s): B2 H12 D128 F128, Tc3 To1, "
-                               "causal, one rehyat_hybrid_fwd call per step",
+        "config": {"workload": f"21x30x52 latent (480x832, 5 s): B2 H12 D128 F{desc.F}, Tc3 "
+                               f"To1, causal, one rehyat_hybrid_fwd call per step"
+                               + ("" if args.phi == "poly2" else f", {phi_label}"),
                    "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)",
                    "y_dtype": "fp32"},
         "tflops": tflops,
