@@ -108,6 +108,9 @@ rehyat_status check_desc(const rehyat_desc* d) {
       return fail(REHYAT_ERR_UNSUPPORTED, "phi_hidden must be 64, 128 or 256 (got %d)", d->phi_hidden);
     if (d->phi_parts < 1 || d->F % d->phi_parts != 0)
       return fail(REHYAT_ERR_SHAPE, "F = %d does not split into phi_parts = %d parts", d->F, d->phi_parts);
+    if (d->F / d->phi_parts < 8)
+      return fail(REHYAT_ERR_UNSUPPORTED, "parts of fewer than 8 features (F = %d, phi_parts = %d)",
+                  d->F, d->phi_parts);
   }
   const int64_t N = (int64_t)d->T * d->HW;
   const int64_t BH = (int64_t)d->B * d->H;

@@ -488,136 +488,208 @@ phi_elu_bf16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ out, 
   reinterpret_cast<u32x4*>(out)[i] = w;
 }
 
-// Transposing stage of rows [0, nrows) x columns [c0, c0+ncols) of src (row length ld, bf16)
-// into dst rows = columns (ncols rows of nrows bf16, row bytes 2*nrows), 16-byte chunk c of a
-// row at chunk c ^ (row & mask). 256 threads.
-__device__ __forceinline__ void stage_t(unsigned char* dst, const uint16_t* src, int ld, int c0,
-                                        int nrows, int ncols, int mask, int tid) {
-  const int cpr = ncols / 8;                 // 8-column pieces per source row
-  for (int id = tid; id < nrows * cpr; id += 256) {
-    const int r = id / cpr, c = id - r * cpr;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(src + (int64_t)r * ld + c0 + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = 8 * c + e;              // destination row = source column
-      const uint16_t hv = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffffu);
-      *reinterpret_cast<uint16_t*>(dst + row * (nrows * 2) + ((((r >> 3) ^ (row & mask))) << 4) +
-                                   ((r & 7) << 1)) = hv;
-    }
-  }
-}
-
-constexpr int kMlpRowTiles = 4;   // 128-row tiles per workgroup
+// Waves per workgroup and features per W2^T slab of the learned map, so that W1^T, one
+// W2^T slab and a 32-row staging buffer per wave fit the 160 KB of LDS, and the registers
+// of two slabs' addressing (F = 256) fit one wave per SIMD.
+template <int F, int HID> struct MlpShape {
+  static constexpr int NW = 4;
+  static constexpr int FS = F < (HID > 128 ? 64 : 128) ? F : (HID > 128 ? 64 : 128);
+};
+constexpr int mlp_threads(int F, int HID) { return 256; }
+constexpr int kMlpRow = 2 * kDim + 16;   // bytes per staged row: 128 bf16 + 16 bytes of pad
+constexpr int kBufWord3 = 0x00020000;    // gfx9 buffer descriptor word 3 (raw, 32-bit data)
+constexpr int kComputeUnits = 256;       // MI355X: one workgroup of the learned map per CU
 
 template <int F, int HID>
-__global__ void __launch_bounds__(256)
+constexpr int mlp_lds_bytes() {
+  return HID * (2 * kDim + 16) + MlpShape<F, HID>::FS * (2 * HID + 16) +
+         MlpShape<F, HID>::NW * 32 * (kMlpRow + 2 * MlpShape<F, HID>::FS + 16) + 4 * (HID + F);
+}
+
+// Rows of W1^T (one hidden unit: 128 d), of W2^T (one feature: HID hidden units) and of the
+// per-wave row buffers are padded by 16 bytes: row strides of 4 mod 64 words keep the 16
+// lanes of a b128 read on distinct banks, and a lane's operand fragments all sit at
+// immediate offsets from one address (rows kappa(l%32) + 32*block, 16-byte chunk
+// 2s + l/32). Each wave owns 32-row tiles; x rows come in and phi rows go out through its
+// buffer with whole-row (coalesced) global accesses. The grid holds as many workgroups as
+// run at once; workgroup g takes the g-th equal share of all heads' tiles, restaging the
+// parameters where its share crosses into another head.
+template <int F, int HID>
+__global__ void __launch_bounds__(mlp_threads(F, HID))
 phi_mlp_bf16_kernel(const uint16_t* __restrict__ x, int64_t n, const uint16_t* __restrict__ params,
-                    int64_t head_elems, int H, int P, uint16_t* __restrict__ out,
-                    int blocks_per_head) {
-  constexpr int FS = F < 128 ? F : 128;
-  constexpr int hid = HID;
-  __shared__ __attribute__((aligned(16))) unsigned char w1t[HID * 256];   // [h][128]
-  __shared__ __attribute__((aligned(16))) unsigned char w2t[FS * HID * 2]; // [FS][h]
+                    int64_t head_elems, int H, int part_shift, uint16_t* __restrict__ out,
+                    int BH) {
+  constexpr int NW = MlpShape<F, HID>::NW;
+  constexpr int FS = MlpShape<F, HID>::FS;
+  constexpr int R1 = kDim * 2 + 16;        // bytes per W1^T row
+  constexpr int R2 = HID * 2 + 16;         // bytes per W2^T row
+  __shared__ __attribute__((aligned(16))) unsigned char w1t[HID * R1];
+  __shared__ __attribute__((aligned(16))) unsigned char w2t[FS * R2];
+  constexpr int RO = 2 * FS + 16;          // bytes per row of a phi staging buffer
+  __shared__ __attribute__((aligned(16))) unsigned char rbuf[NW * 32 * kMlpRow];
+  __shared__ __attribute__((aligned(16))) unsigned char obufs[NW * 32 * RO];
   __shared__ float b1s[HID], b2s[F];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bh = blockIdx.x / blocks_per_head;
-  const int blk = blockIdx.x - bh * blocks_per_head;
-  const uint16_t* p = params + (head_elems ? (int64_t)(bh % H) * head_elems : 0);
-  const uint16_t* W1 = p;
-  const uint16_t* b1 = W1 + (int64_t)kDim * hid;
-  const uint16_t* W2 = b1 + hid;
-  const uint16_t* b2 = W2 + (int64_t)hid * F;
-  const uint16_t* xh = x + (int64_t)bh * n * kDim;
-  uint16_t* oh = out + (int64_t)bh * n * F;
-  constexpr int hmask = (HID / 8 < 16 ? HID / 8 : 16) - 1;
-  // W1^T: rows j (hidden), d chunk at chunk ^ (j & 15) over 16 chunks of 128 d
-  stage_t(w1t, W1, hid, 0, kDim, hid, 15, tid);
-  for (int j = tid; j < hid; j += 256) b1s[j] = bf16_to_f32(((const bf16*)b1)[j]);
-  for (int f = tid; f < F; f += 256) b2s[f] = bf16_to_f32(((const bf16*)b2)[f]);
-  const int part = F / P;
+  unsigned char* buf = rbuf + wave * 32 * kMlpRow;
+  unsigned char* obuf = obufs + wave * 32 * RO;
+  const int a1 = kappa(lane & 31) * R1 + 16 * (lane >> 5);        // W1^T fragment base
+  const int a2 = kappa(lane & 31) * R2 + 16 * (lane >> 5);        // W2^T fragment base
+  const int ax = (lane & 31) * kMlpRow + 16 * (lane >> 5);        // x fragment / phi chunk base
+  const int64_t wtiles = (n + 31) / 32;                           // 32-row tiles per head
+  const int64_t T = (int64_t)BH * wtiles;
+  const int64_t g0 = T * blockIdx.x / gridDim.x, g1 = T * (blockIdx.x + 1) / gridDim.x;
 #pragma unroll 1
-  for (int f0 = 0; f0 < F; f0 += FS) {
-    __syncthreads();
-    stage_t(w2t, W2, F, f0, hid, FS, hmask, tid);   // W2^T slab: rows f, hidden chunks
-    __syncthreads();
-#pragma unroll 1
-    for (int rt = 0; rt < kMlpRowTiles; ++rt) {
-      const int64_t row = ((int64_t)blk * kMlpRowTiles + rt) * 128 + wave * 32 + (lane & 31);
-      const bool ok = row < n;
-      bf16x8 xop[8];
-      {
-        const uint16_t* src = xh + (ok ? row : 0) * kDim + 8 * (lane >> 5);
+  for (int64_t s0 = g0; s0 < g1;) {
+    const int bh = (int)(s0 / wtiles);
+    const int64_t s1 = g1 < (int64_t)(bh + 1) * wtiles ? g1 : (int64_t)(bh + 1) * wtiles;
+    const int64_t tb = (int64_t)bh * wtiles;   // global index of the head's first tile
+    const uint16_t* p = params + (head_elems ? (int64_t)(bh % H) * head_elems : 0);
+    const uint16_t* W1 = p;
+    const uint16_t* b1 = W1 + (int64_t)kDim * HID;
+    const uint16_t* W2 = b1 + HID;
+    const uint16_t* b2 = W2 + (int64_t)HID * F;
+    const uint16_t* xh = x + (int64_t)bh * n * kDim;
+    uint16_t* oh = out + (int64_t)bh * n * F;
+    __syncthreads();   // the previous head's parameters are no longer read
+    for (int id = tid; id < kDim * HID / 8; id += 64 * NW) {     // W1^T
+      const int r = id / (HID / 8), c = id - r * (HID / 8);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(W1 + (int64_t)r * HID + 8 * c);
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          xop[s] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(src + 16 * s) : u32x4{0u, 0u, 0u, 0u});
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(w1t + (8 * c + e) * R1 + 2 * r) =
+            (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffffu);
+    }
+    for (int j = tid; j < HID; j += 64 * NW) b1s[j] = bf16_to_f32(((const bf16*)b1)[j]);
+    for (int f = tid; f < F; f += 64 * NW) b2s[f] = bf16_to_f32(((const bf16*)b2)[f]);
+    // whole-row loads of tile t: piece u = 64 i + lane is row u/16, 16-byte chunk u%16; the
+    // buffer descriptor's range (the head's n rows) turns rows past the end into zeros
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xh, (short)0, (int)(n * kDim * 2), kBufWord3);
+    const __amdgpu_buffer_rsrc_t orr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)oh, (short)0, (int)(n * F * 2), kBufWord3);
+    auto load_rows = [&](int64_t t, u32x4* xg) {
+      const int base = (int)(t - tb) * 32 * kDim * 2 + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        xg[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, base + 1024 * i, 0, 0);
+    };
+#pragma unroll 1
+    for (int f0 = 0; f0 < F; f0 += FS) {
+      if (f0 > 0) __syncthreads();
+      for (int id = tid; id < HID * FS / 8; id += 64 * NW) {     // W2^T slab
+        const int r = id / (FS / 8), c = id - r * (FS / 8);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(W2 + (int64_t)r * F + f0 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(w2t + (8 * c + e) * R2 + 2 * r) =
+              (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffffu);
       }
-      // Hidden block jb (32 units): H^T block, bias, ReLU, bf16; its two 16-unit k-steps go
-      // straight into every output tile of the slab.
-      f32x16 Ps[FS / 32];
+      __syncthreads();
+      // phi rows of the previous tile leave from obuf one tile later, so that their writes
+      // are long done when the wave next waits for its loads (loads and stores share one
+      // counter); stores past the head's last row fall outside the descriptor's range
+      constexpr int CPR = FS / 8;   // 16-byte chunks per row of the slab
+      auto store_rows = [&](int64_t tp) {
 #pragma unroll
-      for (int fb = 0; fb < FS / 32; ++fb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Ps[fb][i] = 0.0f;
+        for (int i = 0; i < 32 * CPR / 64; ++i) {
+          const int u = 64 * i + lane, r = u / CPR, c = u - r * CPR;
+          const int off = ((int)(tp - tb) * 32 + r) * F * 2 + f0 * 2 + 16 * c;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              *reinterpret_cast<const u32x4*>(obuf + r * RO + 16 * c), orr, off, 0, 0);
+        }
+      };
+      u32x4 xg[8];
+      load_rows(s0 + wave, xg);
+      int64_t tprev = -1;
 #pragma unroll 1
-      for (int jb = 0; jb < HID / 32; ++jb) {
+      for (int64_t t = s0 + wave; t < s1; t += NW) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int u = 64 * i + lane;
+          *reinterpret_cast<u32x4*>(buf + (u >> 4) * kMlpRow + 16 * (u & 15)) = xg[i];
+        }
+        if (tprev >= 0) store_rows(tprev);
+        load_rows(t + NW, xg);   // next tile in flight during this one
+        bf16x8 xop[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) xop[s2] = as_bf16x8(lds_read16(buf, ax + 32 * s2));
+        f32x16 Ps[FS / 32];
+#pragma unroll
+        for (int fb = 0; fb < FS / 32; ++fb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) Ps[fb][i] = 0.0f;
+        // hidden block jb (32 units): H^T block (bias, ReLU, bf16) feeds every output tile.
+        // Software-pipelined: block jb+1's dependent chain of 8 MFMAs is interleaved with
+        // block jb's independent output-tile MFMAs.
+        constexpr int NJ = HID / 32;
+        constexpr int L2 = FS / 32 * 2;   // output-tile MFMAs per hidden block
+        auto act = [&](const f32x16& Hc, int jb, bf16x8* hb) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            u32x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i0 = 8 * j + 2 * e;
+              const int u = 32 * jb + cidx(i0, lane);
+              pk[e] = pack_bf16_u32(fmaxf(Hc[i0] + b1s[u], 0.0f), fmaxf(Hc[i0 + 1] + b1s[u + 1], 0.0f));
+            }
+            hb[j] = as_bf16x8(pk);
+          }
+        };
         f32x16 Hc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) Hc[i] = 0.0f;
-        const int arow = 32 * jb + kappa(lane & 31);
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-          const int c = 2 * s2 + (lane >> 5);
-          Hc = mfma32(as_bf16x8(lds_read16(w1t, arow * 256 + ((c ^ (arow & 15)) << 4))), xop[s2], Hc);
-        }
-        bf16x8 hb[2];
+        for (int s2 = 0; s2 < 8; ++s2)
+          Hc = mfma32(as_bf16x8(lds_read16(w1t, a1 + 32 * s2)), xop[s2], Hc);
+#pragma unroll 1
+        for (int jb = 0; jb < NJ - 1; ++jb) {
+          bf16x8 hb[2];
+          act(Hc, jb, hb);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 pk;
+          for (int i = 0; i < 16; ++i) Hc[i] = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i0 = 8 * j + 2 * e;
-            const int u = 32 * jb + cidx(i0, lane);
-            pk[e] = pack_bf16_u32(fmaxf(Hc[i0] + b1s[u], 0.0f), fmaxf(Hc[i0 + 1] + b1s[u + 1], 0.0f));
+          for (int s2 = 0; s2 < (8 > L2 ? 8 : L2); ++s2) {
+            if (s2 < 8)
+              Hc = mfma32(as_bf16x8(lds_read16(w1t, a1 + (jb + 1) * 32 * R1 + 32 * s2)), xop[s2 & 7], Hc);
+            if (s2 < L2)
+              Ps[s2 >> 1] = mfma32(as_bf16x8(lds_read16(w2t, a2 + (s2 >> 1) * 32 * R2 + 64 * jb + 32 * (s2 & 1))),
+                                   hb[s2 & 1], Ps[s2 >> 1]);
           }
-          hb[j] = as_bf16x8(pk);
         }
+        {
+          bf16x8 hb[2];
+          act(Hc, NJ - 1, hb);
+#pragma unroll
+          for (int s2 = 0; s2 < L2; ++s2)
+            Ps[s2 >> 1] = mfma32(as_bf16x8(lds_read16(w2t, a2 + (s2 >> 1) * 32 * R2 + 64 * (NJ - 1) + 32 * (s2 & 1))),
+                                 hb[s2 & 1], Ps[s2 >> 1]);
+        }
+        // phi of the slab's features (bias, the power of the feature's part, bf16) into the
+        // buffer, then out as whole rows
 #pragma unroll
         for (int fb = 0; fb < FS / 32; ++fb) {
-          const int frow = 32 * fb + kappa(lane & 31);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int c = 2 * (2 * jb + j) + (lane >> 5);
-            Ps[fb] = mfma32(as_bf16x8(lds_read16(w2t, frow * (HID * 2) + ((c ^ (frow & hmask)) << 4))),
-                            hb[j], Ps[fb]);
+            // 8 consecutive features of one part (parts hold a multiple of 8 features)
+            const int fl = 32 * fb + 16 * j + 8 * (lane >> 5);
+            float psi[8], v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = psi[e] = Ps[fb][8 * j + e] + b2s[f0 + fl + e];
+            for (int k2 = (f0 + fl) >> part_shift; k2 > 0; --k2)   // part i: psi^i
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] *= psi[e];
+            u32x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = pack_bf16_u32(v[2 * e], v[2 * e + 1]);
+            *reinterpret_cast<u32x4*>(obuf + (lane & 31) * RO + 2 * fl) = pk;
           }
         }
+        tprev = t;
       }
-      // phi of the slab's features: bias, part powers, bf16 rows
-#pragma unroll
-      for (int fb = 0; fb < FS / 32; ++fb) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int fbase = f0 + 32 * fb + 16 * j + 8 * (lane >> 5);
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v2[2];
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-              const int i = 8 * j + 2 * e + q2;
-              const int f = fbase + 2 * e + q2;
-              const float psi = Ps[fb][i] + b2s[f];
-              const int pw = f / part + 1;
-              float v = psi;
-              for (int k2 = 1; k2 < pw; ++k2) v *= psi;
-              v2[q2] = v;
-            }
-            pk[e] = pack_bf16_u32(v2[0], v2[1]);
-          }
-          if (ok) *reinterpret_cast<u32x4*>(oh + row * F + fbase) = pk;
-        }
-      }
+      if (tprev >= 0) store_rows(tprev);
     }
+    s0 = s1;
   }
 }
 
@@ -698,17 +770,27 @@ hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* p
                        (uint16_t*)out, units);
     return hipGetLastError();
   }
-  if (kind != 2 || P < 1 || F % P) return hipErrorInvalidValue;
+  if (kind != 2 || P < 1 || F % P || F / P < 8) return hipErrorInvalidValue;
+  const int part = F / P;                   // F and P are powers of two: part = 2^shift
+  int shift = 0;
+  while ((1 << shift) < part) ++shift;
+  if ((1 << shift) != part) return hipErrorInvalidValue;
   const int64_t head_elems = per_head ? (int64_t)kDim * hid + hid + (int64_t)hid * F + F : 0;
-  const int bph = (int)((n + 128 * kMlpRowTiles - 1) / (128 * kMlpRowTiles));
-  dim3 grid(BH * bph), block(256);
+  // as many workgroups as run at once (1 or 2 per compute unit, by LDS), never more tiles'
+  // worth than there are
+  const int64_t tiles = (int64_t)BH * ((n + 31) / 32);
+  const int64_t wg_max = tiles;
+  dim3 block(mlp_threads(F, hid));
   const uint16_t* xx = (const uint16_t*)x;
   const uint16_t* pp = (const uint16_t*)params;
   uint16_t* oo = (uint16_t*)out;
 #define REHYAT_MLP(FF, HH)                                                                    \
+  static_assert(64 * MlpShape<FF, HH>::NW == mlp_threads(FF, HH), "block size");              \
   if (F == FF && hid == HH) {                                                                 \
+    int64_t nwg = (int64_t)kComputeUnits * (mlp_lds_bytes<FF, HH>() <= 80 * 1024 ? 2 : 1);      \
+    dim3 grid((unsigned)(nwg < wg_max ? nwg : wg_max));                                         \
     hipLaunchKernelGGL((phi_mlp_bf16_kernel<FF, HH>), grid, block, 0, stream, xx, n, pp,        \
-                       head_elems, H, P, oo, bph);                                            \
+                       head_elems, H, shift, oo, BH);                                         \
     return hipGetLastError();                                                                 \
   }
   REHYAT_MLP(64, 64) REHYAT_MLP(64, 128) REHYAT_MLP(64, 256)
@@ -716,7 +798,6 @@ hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* p
   REHYAT_MLP(256, 64) REHYAT_MLP(256, 128) REHYAT_MLP(256, 256)
 #undef REHYAT_MLP
   return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 hipError_t launch_state_partial_phi_bf16(const StateArgs& a, int F, int BH, hipStream_t stream) {

@@ -48,7 +48,8 @@
  *   - Supported sizes: bf16: D = 128, F in {64, 128, 256}. fp32: D in {64, 128},
  *     F in {16, 32, ..., 256} (a multiple of 16). B, H >= 1; T, HW, Tc >= 1; To >= 0;
  *     B*H*T*HW*max(D,F) < 2^31 elements per tensor. phi_kind 1 and 2 need dtype bf16;
- *     phi_kind 2 needs phi_hidden in {64, 128, 256} and F a multiple of phi_parts >= 1.
+ *     phi_kind 2 needs phi_hidden in {64, 128, 256} and F a multiple of phi_parts >= 1
+ *     with parts of at least 8 features (phi_parts <= F/8).
  *   - phi_kind 1 and 2 evaluate phi(q) and phi(k) into the workspace ahead of the attention
  *     and state kernels (bf16 rows); their *_workspace() sizes include those rows.
  */

@@ -164,6 +164,7 @@ def test_feature_map_kind_validation():
     assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=96, phi_parts=2)) == ERR_UNSUP
     assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=0)) == ERR_SHAPE
     assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=3)) == ERR_SHAPE  # 128 % 3
+    assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=32)) == ERR_UNSUP  # 4 per part
     # the fixed map and the learned map need W; 1 + elu has no parameters
     assert fwd(_desc(), Wq=None) == ERR_NULL
     assert fwd(_desc(phi_kind=hs.PHI_MLP, phi_hidden=64, phi_parts=2), Wk=None) == ERR_NULL
