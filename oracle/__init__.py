@@ -19,4 +19,5 @@ from .rehyat_oracle import (  # noqa: F401
     PolyMlpFeatureMap,
     feature,
     feature_dim,
+    hybrid_attention_bwd,
 )

@@ -57,7 +57,7 @@ import numpy as np
 __all__ = [
     "chunk_layout", "phi", "hybrid_attention", "hybrid_attention_bh", "hybrid_recurrent",
     "state_direct", "recurrent_init", "recurrent_step", "EluFeatureMap", "PolyMlpFeatureMap",
-    "feature", "feature_dim",
+    "feature", "feature_dim", "hybrid_attention_bwd",
 ]
 
 
@@ -334,3 +334,101 @@ def recurrent_step(state: Dict[str, object], q_c, k_c, v_c, Wq, Wk, *, HW: int, 
            "k_tail": kw[n_fold:].copy(), "v_tail": vw[n_fold:].copy(),
            "t": int(state["t"]) + 1}
     return y, new
+
+
+# ---------------------------------------------------------------------------------------
+# Backward of the non-recursive form (the training-time form of key design 4, the form the
+# note trains and distils the feature maps with).
+#
+# For one query i, with w_ij its weight of key j (exp(q_i.k_j/sqrt(D)) on the softmax set,
+# phi(q_i).phi(k_j) on the linear set) and den_i = sum_j w_ij:
+#     y_i = sum_j w_ij v_j / den_i.
+# For a loss with upstream gradient dy_i the chain rule gives
+#     dL/dw_ij = dy_i . (v_j - y_i) / den_i,         dL/dv_j += (w_ij / den_i) dy_i,
+# and then, through each kind of weight,
+#     softmax: dL/ds_ij = w_ij dL/dw_ij  ->  dq_i += dL/ds_ij k_j/sqrt(D),
+#                                             dk_j += dL/ds_ij q_i/sqrt(D);
+#     linear:  dphi(q_i) += dL/dw_ij phi(k_j),  dphi(k_j) += dL/dw_ij phi(q_i).
+# Finally through the fixed map phi = 1 + u + u^2/2, u = x W / sqrt(D) (dphi/du = 1 + u):
+#     g = dphi * (1 + u),  dx += g W^T / sqrt(D),  dW += x^T g / sqrt(D).
+# ---------------------------------------------------------------------------------------
+
+def _map_backward(x, W, dphi):
+    """(dx, dW) of the fixed map for rows x, given dL/dphi; (None, None) for map objects."""
+    if callable(W):
+        return None, None
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    D = x.shape[-1]
+    u = (x @ W) / math.sqrt(D)
+    g = dphi * (1.0 + u)
+    return (g @ W.T) / math.sqrt(D), (x.T @ g) / math.sqrt(D)
+
+
+def hybrid_attention_bwd(q, k, v, Wq, Wk, dy, *, HW: int, Tc: int, To: int,
+                         causal: bool = True, block: int = 256) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dy * y) for one (batch, head), y = hybrid_attention(...).
+
+    Returns a dict with dq, dk, dv [N, D]; dphi_q, dphi_k [N, F] (the gradients with
+    respect to the feature rows phi(q_i), phi(k_j)); and, for the fixed map (W matrices),
+    dWq, dWk [D, F]; with the fixed map dq and dk include the path through phi, with a
+    map object they hold the softmax branch only (the map's own backward takes dphi).
+    Queries are processed in blocks of `block` rows with the same sets as the forward.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    N, D = q.shape
+    if N % HW:
+        raise ValueError("N must be a multiple of HW")
+    T = N // HW
+    inv_sqrt_d = 1.0 / math.sqrt(D)
+    phik = feature(k, Wk)
+    F = phik.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dphi_q = np.zeros((N, F))
+    dphi_k = np.zeros((N, F))
+    for (row_lo, row_hi, lo, hi) in chunk_layout(T, HW, Tc, To):
+        Lr = _linear_ranges(lo, hi, N, causal)
+        kS, vS = k[lo:hi], v[lo:hi]
+        for r0 in range(row_lo, row_hi, block):
+            r1 = min(r0 + block, row_hi)
+            Qb, dyb = q[r0:r1], dy[r0:r1]
+            # forward weights of the block, as in hybrid_attention
+            ES = np.exp((Qb @ kS.T) * inv_sqrt_d)
+            num = ES @ vS
+            den = ES.sum(axis=1)
+            pq = feature(Qb, Wq) if Lr else None
+            EL = []
+            for (a, b) in Lr:
+                E = pq @ phik[a:b].T
+                EL.append(E)
+                num = num + E @ v[a:b]
+                den = den + E.sum(axis=1)
+            yb = num / den[:, None]
+            # dL/dw_ij = g_i . v_j - c_i with g_i = dy_i / den_i, c_i = dy_i . y_i / den_i
+            g = dyb / den[:, None]
+            c = (dyb * yb).sum(axis=1) / den
+            dW_S = g @ vS.T - c[:, None]
+            dS = dW_S * ES
+            dq[r0:r1] += (dS @ kS) * inv_sqrt_d
+            dk[lo:hi] += (dS.T @ Qb) * inv_sqrt_d
+            dv[lo:hi] += ES.T @ g
+            for (a, b), E in zip(Lr, EL):
+                dW_L = g @ v[a:b].T - c[:, None]
+                dphi_q[r0:r1] += dW_L @ phik[a:b]
+                dphi_k[a:b] += dW_L.T @ pq
+                dv[a:b] += E.T @ g
+    out = {"dq": dq, "dk": dk, "dv": dv, "dphi_q": dphi_q, "dphi_k": dphi_k}
+    dxq, dWq = _map_backward(q, Wq, dphi_q)
+    dxk, dWk = _map_backward(k, Wk, dphi_k)
+    if dxq is not None:
+        out["dq"] = dq + dxq
+        out["dWq"] = dWq
+    if dxk is not None:
+        out["dk"] = dk + dxk
+        out["dWk"] = dWk
+    return out
