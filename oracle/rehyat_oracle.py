@@ -353,20 +353,10 @@ def recurrent_step(state: Dict[str, object], q_c, k_c, v_c, Wq, Wk, *, HW: int, 
 #     g = dphi * (1 + u),  dx += g W^T / sqrt(D),  dW += x^T g / sqrt(D).
 # ---------------------------------------------------------------------------------------
 
-def _map_backward(x, W, dphi):
-    """(dx, dW) of the fixed map for rows x, given dL/dphi; (None, None) for map objects."""
-    if callable(W):
-        return None, None
-    x = np.asarray(x, dtype=np.float64)
-    W = np.asarray(W, dtype=np.float64)
-    D = x.shape[-1]
-    u = (x @ W) / math.sqrt(D)
-    g = dphi * (1.0 + u)
-    return (g @ W.T) / math.sqrt(D), (x.T @ g) / math.sqrt(D)
-
-
 def hybrid_attention_bwd(q, k, v, Wq, Wk, dy, *, HW: int, Tc: int, To: int,
-                         causal: bool = True, block: int = 256) -> Dict[str, np.ndarray]:
+                         causal: bool = True, block: int = 256,
+                         rows: Optional[Sequence[int]] = None,
+                         keys: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Gradients of sum(dy * y) for one (batch, head), y = hybrid_attention(...).
 
     Returns a dict with dq, dk, dv [N, D]; dphi_q, dphi_k [N, F] (the gradients with
@@ -374,6 +364,11 @@ def hybrid_attention_bwd(q, k, v, Wq, Wk, dy, *, HW: int, Tc: int, To: int,
     dWq, dWk [D, F]; with the fixed map dq and dk include the path through phi, with a
     map object they hold the softmax branch only (the map's own backward takes dphi).
     Queries are processed in blocks of `block` rows with the same sets as the forward.
+
+    rows / keys: optional subsets. Only the query rows in `rows` get dq and dphi_q and only
+    the keys in `keys` get dk, dv and dphi_k (other entries are NaN; an empty list skips
+    that side); dWq needs every row and dWk every key, so each is returned only when its
+    side is complete. The sums are the same; only the entries asked for are formed.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -386,6 +381,8 @@ def hybrid_attention_bwd(q, k, v, Wq, Wk, dy, *, HW: int, Tc: int, To: int,
     inv_sqrt_d = 1.0 / math.sqrt(D)
     phik = feature(k, Wk)
     F = phik.shape[1]
+    row_on = np.ones(N, dtype=bool) if rows is None else np.isin(np.arange(N), np.asarray(rows, dtype=np.int64))
+    key_on = np.ones(N, dtype=bool) if keys is None else np.isin(np.arange(N), np.asarray(keys, dtype=np.int64))
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -394,8 +391,15 @@ def hybrid_attention_bwd(q, k, v, Wq, Wk, dy, *, HW: int, Tc: int, To: int,
     for (row_lo, row_hi, lo, hi) in chunk_layout(T, HW, Tc, To):
         Lr = _linear_ranges(lo, hi, N, causal)
         kS, vS = k[lo:hi], v[lo:hi]
+        # keys of each set whose gradients are asked for
+        ks_sel = np.nonzero(key_on[lo:hi])[0]
+        kl_sel = [np.nonzero(key_on[a:b])[0] for (a, b) in Lr]
+        any_keys = ks_sel.size > 0 or any(x.size for x in kl_sel)
         for r0 in range(row_lo, row_hi, block):
             r1 = min(r0 + block, row_hi)
+            rsel = np.nonzero(row_on[r0:r1])[0]
+            if rsel.size == 0 and not any_keys:
+                continue
             Qb, dyb = q[r0:r1], dy[r0:r1]
             # forward weights of the block, as in hybrid_attention
             ES = np.exp((Qb @ kS.T) * inv_sqrt_d)
@@ -412,23 +416,37 @@ def hybrid_attention_bwd(q, k, v, Wq, Wk, dy, *, HW: int, Tc: int, To: int,
             # dL/dw_ij = g_i . v_j - c_i with g_i = dy_i / den_i, c_i = dy_i . y_i / den_i
             g = dyb / den[:, None]
             c = (dyb * yb).sum(axis=1) / den
-            dW_S = g @ vS.T - c[:, None]
-            dS = dW_S * ES
-            dq[r0:r1] += (dS @ kS) * inv_sqrt_d
-            dk[lo:hi] += (dS.T @ Qb) * inv_sqrt_d
-            dv[lo:hi] += ES.T @ g
-            for (a, b), E in zip(Lr, EL):
-                dW_L = g @ v[a:b].T - c[:, None]
-                dphi_q[r0:r1] += dW_L @ phik[a:b]
-                dphi_k[a:b] += dW_L.T @ pq
-                dv[a:b] += E.T @ g
+            # softmax set: dL/ds_ij = w_ij dL/dw_ij
+            if rsel.size:
+                dS_r = (g[rsel] @ vS.T - c[rsel, None]) * ES[rsel]
+                dq[r0 + rsel] += (dS_r @ kS) * inv_sqrt_d
+            if ks_sel.size:
+                dS_k = (g @ vS[ks_sel].T - c[:, None]) * ES[:, ks_sel]
+                dk[lo + ks_sel] += (dS_k.T @ Qb) * inv_sqrt_d
+                dv[lo + ks_sel] += ES[:, ks_sel].T @ g
+            # linear set: dphi(q_i) += dL/dw_ij phi(k_j), dphi(k_j) += dL/dw_ij phi(q_i)
+            for (a, b), E, ksel in zip(Lr, EL, kl_sel):
+                if rsel.size:
+                    dW_r = g[rsel] @ v[a:b].T - c[rsel, None]
+                    dphi_q[r0 + rsel] += dW_r @ phik[a:b]
+                if ksel.size:
+                    dW_k = g @ v[a + ksel].T - c[:, None]
+                    dphi_k[a + ksel] += dW_k.T @ pq
+                    dv[a + ksel] += E[:, ksel].T @ g
+    dq[~row_on] = np.nan
+    dphi_q[~row_on] = np.nan
+    for arr in (dk, dv, dphi_k):
+        arr[~key_on] = np.nan
     out = {"dq": dq, "dk": dk, "dv": dv, "dphi_q": dphi_q, "dphi_k": dphi_k}
-    dxq, dWq = _map_backward(q, Wq, dphi_q)
-    dxk, dWk = _map_backward(k, Wk, dphi_k)
-    if dxq is not None:
-        out["dq"] = dq + dxq
-        out["dWq"] = dWq
-    if dxk is not None:
-        out["dk"] = dk + dxk
-        out["dWk"] = dWk
+    for side, x, W, on in (("q", q, Wq, row_on), ("k", k, Wk, key_on)):
+        if callable(W):
+            continue
+        W = np.asarray(W, dtype=np.float64)
+        dphi = out["dphi_" + side]
+        sel = np.nonzero(on)[0]
+        u = (x[sel] @ W) / math.sqrt(D)
+        gx = dphi[sel] * (1.0 + u)
+        out["d" + side][sel] += (gx @ W.T) / math.sqrt(D)
+        if on.all():
+            out["dW" + side] = (x.T @ gx) / math.sqrt(D)
     return out

@@ -91,3 +91,22 @@ def test_each_planted_backward_mistake_fails_a_pin(bug):
         if not err < 1e-6:
             caught.append(name)
     assert caught, f"no pin catches {bug}"
+
+
+def test_backward_subsets_match_full():
+    """rows / keys restrict which entries are formed, not the sums."""
+    rng = np.random.default_rng(5)
+    T, HW, D, F, Tc, To = 7, 5, 6, 4, 2, 1
+    N = T * HW
+    q, k, v, dy = (rng.normal(size=(N, D)) for _ in range(4))
+    Wq, Wk = 0.3 * rng.normal(size=(D, F)), 0.3 * rng.normal(size=(D, F))
+    for causal in (True, False):
+        full = orc.hybrid_attention_bwd(q, k, v, Wq, Wk, dy, HW=HW, Tc=Tc, To=To, causal=causal)
+        rows, keys = [0, 3, 11, 20, 34], [1, 9, 10, 22, 33]
+        sub = orc.hybrid_attention_bwd(q, k, v, Wq, Wk, dy, HW=HW, Tc=Tc, To=To, causal=causal,
+                                       rows=rows, keys=keys, block=4)
+        for name, sel in (("dq", rows), ("dphi_q", rows), ("dk", keys), ("dv", keys),
+                          ("dphi_k", keys)):
+            assert np.allclose(sub[name][sel], full[name][sel], rtol=1e-12, atol=1e-12), name
+        assert "dWq" not in sub and "dWk" not in sub
+        assert np.isnan(sub["dq"][1]).all() and np.isnan(sub["dk"][0]).all()
