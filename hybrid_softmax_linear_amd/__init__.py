@@ -6,7 +6,8 @@ memory and the current HIP stream. There is no CPU fallback: if the library is m
 a call fails, an exception is raised.
 
 The functions carry the names of the C entry points (include/rehyat.h):
-    rehyat_phi, rehyat_state_update, rehyat_hybrid_fwd, rehyat_recurrent_step
+    rehyat_phi, rehyat_state_update, rehyat_hybrid_fwd, rehyat_hybrid_fwd_stats,
+    rehyat_hybrid_bwd, rehyat_recurrent_step
 plus *_workspace helpers, rehyat_timing_enable / rehyat_timing_read.
 """
 from __future__ import annotations
@@ -21,6 +22,7 @@ __all__ = [
     "rehyat_phi", "rehyat_state_update", "rehyat_state_update_workspace",
     "rehyat_hybrid_fwd", "rehyat_hybrid_fwd_workspace",
     "rehyat_recurrent_step", "rehyat_recurrent_step_workspace",
+    "rehyat_hybrid_fwd_stats", "rehyat_hybrid_bwd", "rehyat_hybrid_bwd_workspace",
     "rehyat_timing_enable", "rehyat_timing_read", "F32", "BF16", "CAUSAL", "BIDIR",
     "PHI_POLY2", "PHI_ELU", "PHI_MLP",
 ]
@@ -97,6 +99,11 @@ _SIGS = {
     "rehyat_recurrent_step_workspace": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
     "rehyat_recurrent_step": (ctypes.c_int, [ctypes.POINTER(_CDesc), ctypes.c_int32] +
                               [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "rehyat_hybrid_fwd_stats": (ctypes.c_int, [ctypes.POINTER(_CDesc)] + [ctypes.c_void_p] * 8 +
+                                [ctypes.c_size_t, ctypes.c_void_p]),
+    "rehyat_hybrid_bwd_workspace": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
+    "rehyat_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(_CDesc)] + [ctypes.c_void_p] * 14 +
+                          [ctypes.c_size_t, ctypes.c_void_p]),
     "rehyat_timing_enable": (ctypes.c_int, [ctypes.c_int32]),
     "rehyat_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]),
@@ -179,6 +186,31 @@ def rehyat_hybrid_fwd(desc: Desc, q, k, v, Wq, Wk, y, ws, ws_bytes: Optional[int
     _check(lib().rehyat_hybrid_fwd(ctypes.byref(desc.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(Wq),
                                    _ptr(Wk), _ptr(y), _ptr(ws), nb, _stream(stream)),
            "rehyat_hybrid_fwd")
+
+
+def rehyat_hybrid_fwd_stats(desc: Desc, q, k, v, Wq, Wk, y, lse, ws,
+                            ws_bytes: Optional[int] = None, stream=None) -> None:
+    """rehyat_hybrid_fwd that also writes lse = log2 of each row's normaliser."""
+    nb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(lib().rehyat_hybrid_fwd_stats(ctypes.byref(desc.c()), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(Wq), _ptr(Wk), _ptr(y), _ptr(lse), _ptr(ws), nb,
+                                         _stream(stream)),
+           "rehyat_hybrid_fwd_stats")
+
+
+def rehyat_hybrid_bwd_workspace(desc: Desc) -> int:
+    return int(lib().rehyat_hybrid_bwd_workspace(ctypes.byref(desc.c())))
+
+
+def rehyat_hybrid_bwd(desc: Desc, q, k, v, Wq, Wk, y, lse, dy, dq, dk, dv, dWq, dWk, ws,
+                      ws_bytes: Optional[int] = None, stream=None) -> None:
+    """Gradients of sum(dy * y) of the causal form (see include/rehyat.h)."""
+    nb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(lib().rehyat_hybrid_bwd(ctypes.byref(desc.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(Wq),
+                                   _ptr(Wk), _ptr(y), _ptr(lse), _ptr(dy), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(dWq), _ptr(dWk), _ptr(ws), nb,
+                                   _stream(stream)),
+           "rehyat_hybrid_bwd")
 
 
 def rehyat_recurrent_step_workspace(desc: Desc) -> int:

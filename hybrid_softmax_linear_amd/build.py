@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librehyat.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_bf16.hip", "state_bf16.hip", "reduce.hip", "f32_path.hip", "api.cpp"]
+SOURCES = ["attn_bf16.hip", "state_bf16.hip", "reduce.hip", "f32_path.hip", "bwd_bf16.hip", "api.cpp"]
 
 # Packed fp32 VALU ops are switched off for all device code (ordinary fp32 math only).
 FLAGS = [

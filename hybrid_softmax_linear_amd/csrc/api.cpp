@@ -40,6 +40,18 @@ hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* p
                                int per_head, int H, int hid, int P, int BH, int F, void* out,
                                hipStream_t stream);
 hipError_t launch_state_partial_phi_bf16(const StateArgs& a, int F, int BH, hipStream_t stream);
+hipError_t launch_bwd_prep(const void* y, const void* dy, int y_f32, const float* lse, int64_t rows,
+                           uint16_t* dyb, uint16_t* gb, float* cvec, float* dvec,
+                           hipStream_t stream);
+hipError_t launch_state_rows_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH, int F,
+                                  uint16_t* img, hipStream_t stream);
+hipError_t launch_transpose_w(const void* W, int F, int nW, uint16_t* Wt, hipStream_t stream);
+hipError_t launch_suffix_states(const float* part, float* out, int F, int D, int T, int Tc, int To,
+                                int BH, hipStream_t stream);
+hipError_t launch_dw_finalize(const float* parts, int64_t E, int BH, int H, int per_head, int F,
+                              float* dW, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int F, int nblocks, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int F, int nblocks, hipStream_t stream);
 }  // namespace rehyat
 
 using namespace rehyat;
@@ -240,6 +252,34 @@ size_t step_gather_bytes(const rehyat_desc* d) {
   return BH * (size_t)step_nk_max(d) * d->D * 2 + BH * d->D * (size_t)step_vt_ld(d) * 2;
 }
 
+rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k, const void* v,
+                              const void* Wq, const void* Wk, void* y, float* lse, void* ws,
+                              size_t ws_bytes, void* stream);
+
+// Workspace of rehyat_hybrid_bwd, regions in this order (each rounded to 256 bytes).
+struct BwdLayout {
+  size_t part, states, gst, simg, gimg, wtq, wtk, dyb, gb, cvec, dvec, phiq, gq, gk, dws, dwz;
+  size_t total;
+};
+
+BwdLayout bwd_layout(const rehyat_desc* d) {
+  const size_t BH = (size_t)d->B * d->H, N = (size_t)d->T * d->HW, T = d->T;
+  const size_t nch = n_chunks(d), E = state_elems(d), F = d->F, D = d->D;
+  const size_t nW = d->w_per_head ? d->H : 1;
+  const size_t sizes[16] = {BH * T * E * 4,   BH * nch * E * 4, BH * T * E * 4,  BH * nch * F * D * 2,
+                            BH * T * F * D * 2, nW * F * D * 2,  nW * F * D * 2,  BH * N * D * 2,
+                            BH * N * D * 2,   BH * N * 4,       BH * N * 4,      BH * N * F * 2,
+                            BH * N * F * 2,   BH * N * F * 2,   BH * F * D * 4,  BH * F * 4};
+  size_t off[16], o = 0;
+  for (int i = 0; i < 16; ++i) {
+    off[i] = o;
+    o += (sizes[i] + 255) / 256 * 256;
+  }
+  BwdLayout L{off[0], off[1], off[2], off[3], off[4], off[5], off[6], off[7],
+              off[8], off[9], off[10], off[11], off[12], off[13], off[14], off[15], o};
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,6 +393,23 @@ size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* d) {
 rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
                                 const void* Wq, const void* Wk, void* y, void* ws, size_t ws_bytes,
                                 void* stream) {
+  return hybrid_fwd_impl(d, q, k, v, Wq, Wk, y, nullptr, ws, ws_bytes, stream);
+}
+
+rehyat_status rehyat_hybrid_fwd_stats(const rehyat_desc* d, const void* q, const void* k,
+                                      const void* v, const void* Wq, const void* Wk, void* y,
+                                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!lse) return fail(REHYAT_ERR_NULL, "lse must be non-NULL");
+  return hybrid_fwd_impl(d, q, k, v, Wq, Wk, y, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k, const void* v,
+                              const void* Wq, const void* Wk, void* y, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
   rehyat_status st = check_desc(d);
   if (st != REHYAT_OK) return st;
   if (!q || !k || !v || (needs_w(d) && (!Wq || !Wk)) || !y)
@@ -372,6 +429,13 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
       overlaps(y, ny, Wq, nw) || overlaps(y, ny, Wk, nw) || overlaps(ws, need, y, ny) ||
       overlaps(ws, need, q, nin) || overlaps(ws, need, k, nin) || overlaps(ws, need, v, nin))
     return fail(REHYAT_ERR_ALIAS, "y, workspace and inputs must not overlap");
+  if (lse) {
+    const size_t nl = (size_t)BH * N * sizeof(float);
+    if (!aligned16(lse)) return fail(REHYAT_ERR_ALIGN, "lse must be 16-byte aligned");
+    if (overlaps(lse, nl, y, ny) || overlaps(lse, nl, q, nin) || overlaps(lse, nl, k, nin) ||
+        overlaps(lse, nl, v, nin) || overlaps(lse, nl, ws, need))
+      return fail(REHYAT_ERR_ALIAS, "lse must not overlap y, the inputs or the workspace");
+  }
 
   hipStream_t s = (hipStream_t)stream;
   const int nch = n_chunks(d);
@@ -442,6 +506,7 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
   a.st_img = simg; a.st_img_bh = (int64_t)(nch * image_bytes(d)); a.st_img_t = (int64_t)image_bytes(d);
   a.phiq = (phi_ahead(d) && need_state) ? phiq : nullptr;
+  a.lse = lse;
   a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
   a.n_chunks = nch; a.chunk0 = 0; a.step = 0;
   a.bidir = d->mode == REHYAT_BIDIR;
@@ -452,6 +517,10 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void*
   a.u_scale = us;
   return hip_status(launch_attention(d, a, s), "attention launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t rehyat_recurrent_step_workspace(const rehyat_desc* d) {
   if (check_desc(d) != REHYAT_OK) return 0;
@@ -597,6 +666,155 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
     e = launch_copy_rows(k_c, v_c, k_tail, v_tail, crow, crow - trow, trow, (int)(d->D * es), BH, s);
     if (e != hipSuccess) return hip_status(e, "tail copy launch");
   }
+  return ok();
+}
+
+size_t rehyat_hybrid_bwd_workspace(const rehyat_desc* d) {
+  if (check_desc(d) != REHYAT_OK) return 0;
+  return bwd_layout(d).total;
+}
+
+rehyat_status rehyat_hybrid_bwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
+                                const void* Wq, const void* Wk, const void* y, const float* lse,
+                                const void* dy, float* dq, float* dk, float* dv, float* dWq,
+                                float* dWk, void* ws, size_t ws_bytes, void* stream) {
+  rehyat_status st = check_desc(d);
+  if (st != REHYAT_OK) return st;
+  if (d->dtype != REHYAT_BF16 || d->phi_kind != REHYAT_PHI_POLY2)
+    return fail(REHYAT_ERR_UNSUPPORTED, "the backward supports bf16 inputs with the fixed feature map");
+  if (d->mode != REHYAT_CAUSAL)
+    return fail(REHYAT_ERR_UNSUPPORTED, "the backward supports the causal form");
+  const void* ins[8] = {q, k, v, Wq, Wk, y, lse, dy};
+  const void* outs[5] = {dq, dk, dv, dWq, dWk};
+  for (const void* p : ins)
+    if (!p) return fail(REHYAT_ERR_NULL, "q, k, v, Wq, Wk, y, lse, dy must be non-NULL");
+  for (const void* p : outs)
+    if (!p) return fail(REHYAT_ERR_NULL, "dq, dk, dv, dWq, dWk must be non-NULL");
+  for (const void* p : ins)
+    if (!aligned16(p)) return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+  for (const void* p : outs)
+    if (!aligned16(p)) return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+  const BwdLayout L = bwd_layout(d);
+  if (!ws || ws_bytes < L.total)
+    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
+  const int BH = d->B * d->H;
+  const int64_t N = (int64_t)d->T * d->HW;
+  const int F = d->F, D = d->D, T = d->T, nch = n_chunks(d);
+  const size_t nin = (size_t)BH * N * D * 2, nyb = (size_t)BH * N * D * esize(d->y_dtype);
+  const size_t nd = (size_t)BH * N * D * 4, nl = (size_t)BH * N * 4;
+  const size_t nwb = w_bytes(d), nwo = (size_t)(d->w_per_head ? d->H : 1) * D * F * 4;
+  const void* in_p[8] = {q, k, v, Wq, Wk, y, lse, dy};
+  const size_t in_n[8] = {nin, nin, nin, nwb, nwb, nyb, nl, nyb};
+  void* out_p[6] = {dq, dk, dv, dWq, dWk, ws};
+  const size_t out_n[6] = {nd, nd, nd, nwo, nwo, L.total};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(out_p[i], out_n[i], in_p[j], in_n[j]))
+        return fail(REHYAT_ERR_ALIAS, "outputs and workspace must not overlap the inputs");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(out_p[i], out_n[i], out_p[j], out_n[j]))
+        return fail(REHYAT_ERR_ALIAS, "outputs and workspace must not overlap each other");
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char* w8 = reinterpret_cast<unsigned char*>(ws);
+  float* part = reinterpret_cast<float*>(w8 + L.part);
+  float* states = reinterpret_cast<float*>(w8 + L.states);
+  float* gst = reinterpret_cast<float*>(w8 + L.gst);
+  uint16_t* simg = reinterpret_cast<uint16_t*>(w8 + L.simg);
+  uint16_t* gimg = reinterpret_cast<uint16_t*>(w8 + L.gimg);
+  uint16_t* wtq = reinterpret_cast<uint16_t*>(w8 + L.wtq);
+  uint16_t* wtk = reinterpret_cast<uint16_t*>(w8 + L.wtk);
+  uint16_t* dyb = reinterpret_cast<uint16_t*>(w8 + L.dyb);
+  uint16_t* gb = reinterpret_cast<uint16_t*>(w8 + L.gb);
+  float* cvec = reinterpret_cast<float*>(w8 + L.cvec);
+  float* dvec = reinterpret_cast<float*>(w8 + L.dvec);
+  uint16_t* phiq = reinterpret_cast<uint16_t*>(w8 + L.phiq);
+  uint16_t* gq = reinterpret_cast<uint16_t*>(w8 + L.gq);
+  uint16_t* gk = reinterpret_cast<uint16_t*>(w8 + L.gk);
+  float* dws = reinterpret_cast<float*>(w8 + L.dws);
+  float* dwz = reinterpret_cast<float*>(w8 + L.dwz);
+  const int64_t E = (int64_t)state_elems(d);
+  const float us = 1.0f / std::sqrt((float)D);
+  const int nW = d->w_per_head ? d->H : 1;
+  hipError_t e;
+#define REHYAT_TRY(call, what) \
+  do {                         \
+    e = (call);                \
+    if (e != hipSuccess) return hip_status(e, what); \
+  } while (0)
+
+  // 1. forward states S_t, z_t of every chunk (as in the forward)
+  {
+    StateArgs sa{};
+    sa.ka = k; sa.va = v; sa.a_rows = N; sa.a_row0 = 0;
+    sa.kb = k; sa.vb = v; sa.b_rows = N; sa.b_row0 = 0;
+    sa.na = N; sa.n = N; sa.seg_len = d->HW; sa.n_seg = T;
+    sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
+    sa.part = part; sa.u_scale = us;
+    REHYAT_TRY(launch_partial(d, sa, s), "state partial launch");
+    REHYAT_TRY(launch_scan_states(part, states, F, D, T, d->Tc, d->To, nch, 0, BH, s), "state scan launch");
+    REHYAT_TRY(launch_state_rows_bf16(states, nch * E, E, nch, BH, F, simg, s), "state image launch");
+  }
+  REHYAT_TRY(launch_transpose_w(Wq, F, nW, wtq, s), "transpose launch");
+  REHYAT_TRY(launch_transpose_w(Wk, F, nW, wtk, s), "transpose launch");
+  // 2. per-row dy.y, dy / den
+  REHYAT_TRY(launch_bwd_prep(y, dy, d->y_dtype == REHYAT_F32, lse, (int64_t)BH * N, dyb, gb, cvec, dvec, s),
+             "prep launch");
+  // 3. dq (window and linear read-out), phi(q) and gq rows
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dyb = dyb; a.gb = gb; a.lse = lse; a.cvec = cvec; a.dvec = dvec;
+  a.w_per_head = d->w_per_head;
+  a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = T; a.N = (int)N; a.n_chunks = nch;
+  a.logit_scale = kLog2e * us; a.u_scale = us;
+  const int64_t Np = (int64_t)d->Tc * d->HW;
+  const int last_rows = (int)(N - (int64_t)(nch - 1) * Np);
+  {
+    BwdArgs b = a;
+    b.w = reinterpret_cast<const uint16_t*>(Wq); b.wt = wtq;
+    b.st_img = simg; b.st = states; b.nslot = nch;
+    b.dx = dq; b.phi_out = phiq; b.g_out = gq;
+    b.tiles_per_chunk = (int)((Np + 255) / 256);
+    b.tiles_last = (last_rows + 255) / 256;
+    b.tiles_per_head = (nch - 1) * b.tiles_per_chunk + b.tiles_last;
+    REHYAT_TRY(launch_bwd_dq(b, F, BH * b.tiles_per_head, s), "dq launch");
+  }
+  // 4. reverse states: per query frame sums phi(q) g^T and phi(q) c, suffix over chunks
+  {
+    StateArgs sa{};
+    sa.ka = gb; sa.va = gb; sa.a_rows = N; sa.a_row0 = 0;
+    sa.kb = gb; sa.vb = gb; sa.b_rows = N; sa.b_row0 = 0;
+    sa.na = N; sa.n = N; sa.seg_len = d->HW; sa.n_seg = T;
+    sa.part = part; sa.phik = phiq; sa.phik_rows = N; sa.zw = cvec;
+    REHYAT_TRY(launch_state_partial_phi_bf16(sa, F, BH, s), "reverse state launch");
+    REHYAT_TRY(launch_suffix_states(part, gst, F, D, T, d->Tc, d->To, BH, s), "suffix launch");
+    REHYAT_TRY(launch_state_rows_bf16(gst, T * E, E, T, BH, F, gimg, s), "state image launch");
+  }
+  // 5. dk, dv (window and linear parts), gk rows
+  {
+    BwdArgs b = a;
+    b.w = reinterpret_cast<const uint16_t*>(Wk); b.wt = wtk;
+    b.st_img = gimg; b.st = gst; b.nslot = T;
+    b.dx = dk; b.dv = dv; b.g_out = gk;
+    b.tiles_per_chunk = (int)((Np + 127) / 128);
+    b.tiles_last = (last_rows + 127) / 128;
+    b.tiles_per_head = (nch - 1) * b.tiles_per_chunk + b.tiles_last;
+    REHYAT_TRY(launch_bwd_dkdv(b, F, BH * b.tiles_per_head, s), "dk/dv launch");
+  }
+  // 6. dW = sum over rows of x gx^T (per frame, folded per head, summed over heads / batch)
+  for (int side = 0; side < 2; ++side) {
+    StateArgs sa{};
+    const void* x = side ? k : q;
+    sa.ka = x; sa.va = x; sa.a_rows = N; sa.a_row0 = 0;
+    sa.kb = x; sa.vb = x; sa.b_rows = N; sa.b_row0 = 0;
+    sa.na = N; sa.n = N; sa.seg_len = d->HW; sa.n_seg = T;
+    sa.part = part; sa.phik = side ? gk : gq; sa.phik_rows = N;
+    REHYAT_TRY(launch_state_partial_phi_bf16(sa, F, BH, s), "dW partial launch");
+    REHYAT_TRY(launch_fold_states(part, T, dws, dwz, F, D, 1, BH, s), "dW fold launch");
+    REHYAT_TRY(launch_dw_finalize(dws, (int64_t)F * D, BH, d->H, d->w_per_head, F, side ? dWk : dWq, s),
+               "dW finalize launch");
+  }
+#undef REHYAT_TRY
   return ok();
 }
 

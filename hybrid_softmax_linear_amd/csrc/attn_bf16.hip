@@ -589,7 +589,10 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: y = O / l ------------------------------------------------------------
-  const float inv = 1.0f / pair_sum(A.l);
+  const float ltot = pair_sum(A.l);
+  const float inv = 1.0f / ltot;
+  if (a.lse && active && qrow < g.rows && lane < 32)
+    a.lse[(int64_t)g.bh * a.q_rows + g.q_row_base + qrow] = m0 + fast_log2(ltot);
   if (active && qrow < g.rows) {
     const int64_t off = head_off(g.bh, a.q_rows, kDim) + (g.q_row_base + qrow) * kDim;
 #pragma unroll

@@ -140,6 +140,9 @@ struct AttnArgs {
   // bf16 path, feature maps computed ahead (learned / elu maps): phi(q) rows [.][q_rows][F]
   // with the same row indexing as q; NULL: phi(q) = 1 + u + u^2/2 computed in the kernel
   const void* phiq;
+  // optional per-row statistic: log2 of the row's joint normaliser n^S + n^L (softmax
+  // weights exp(q.k/sqrt(D))), same row indexing as q; NULL: not written
+  float* lse;
   int H;
   int HW, Tc, To, T;    // geometry of the whole video
   int n_chunks;         // chunks handled by this launch
@@ -153,6 +156,31 @@ struct AttnArgs {
   int nblocks;
   float logit_scale;    // log2(e) / sqrt(D)
   float u_scale;        // 1 / sqrt(D)
+};
+
+// Backward of the non-recursive form, bf16 path (bwd_bf16.hip). Rows are [BH][N][128]
+// unless noted.
+struct BwdArgs {
+  const void* q; const void* k; const void* v;   // bf16 inputs of the forward
+  const uint16_t* dyb;      // dy rounded to bf16
+  const uint16_t* gb;       // dy / den rounded to bf16 (den = the row's joint normaliser)
+  const float* lse;         // [BH][N] log2(den)
+  const float* cvec;        // [BH][N] (dy . y) / den
+  const float* dvec;        // [BH][N] dy . y
+  const uint16_t* w;        // the map's W [nW][128][F] (q side in the dq kernel, k side in dkdv)
+  const uint16_t* wt;       // its transpose [nW][F][128]
+  int w_per_head;
+  const uint16_t* st_img;   // bf16 rows [F][128] of per-slot states: + (bh * nslot + slot) * F * 128
+  const float* st;          // the fp32 states (F*128 + F floats each), same slots, for z / h
+  int nslot;
+  float* dx;                // dq (dq kernel) or dk (dkdv kernel), fp32
+  float* dv;                // dkdv kernel: dv, fp32
+  uint16_t* phi_out;        // dq kernel: phi(q) rows [BH][N][F] bf16
+  uint16_t* g_out;          // rows [BH][N][F] bf16 of dphi * (1 + u) / sqrt(D)
+  int H, HW, Tc, To, T, N, n_chunks;
+  int tiles_per_chunk, tiles_last, tiles_per_head;
+  float logit_scale;        // log2(e) / sqrt(D)
+  float u_scale;            // 1 / sqrt(D)
 };
 
 // Per-segment partial states: one workgroup per (head, segment).
@@ -170,6 +198,9 @@ struct StateArgs {
   // optional (bf16 path): phi(k) computed ahead, virtual row w of head bh at
   // phik + (bh * phik_rows + w) * F; NULL: phi(k) = 1 + u + u^2/2 from Wk in the kernel
   const void* phik; int64_t phik_rows;
+  // optional per-row weights of the z sums (phi rows path only): z += sum_r zw[r] phi(k_r),
+  // zw + bh * phik_rows + r; NULL: z += sum_r phi(k_r)
+  const float* zw;
 };
 
 }  // namespace rehyat

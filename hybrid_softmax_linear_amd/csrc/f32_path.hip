@@ -142,6 +142,7 @@ hybrid_attn_f32_kernel(AttnArgs a, int F) {
   }
   if (qok) {
     const float inv = 1.0f / l;
+    if (a.lse && p == 0) a.lse[(int64_t)bh * a.q_rows + q_row_base + qrow] = m + fast_log2(l);
     const int64_t off = head_off(bh, a.q_rows, D) + (q_row_base + qrow) * D + p * DS;
 #pragma unroll
     for (int e = 0; e < DS; ++e) {

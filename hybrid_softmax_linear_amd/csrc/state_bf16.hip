@@ -341,6 +341,7 @@ state_partial_phi_bf16_kernel(StateArgs a) {
   constexpr int PIT = kTileRows * PPR / 256;         // phi pieces per thread and tile
   __shared__ __attribute__((aligned(16))) unsigned char pt[kTileRows * PLD];
   __shared__ __attribute__((aligned(16))) unsigned char vt[kVTileBytes];
+  __shared__ float zws[kTileRows];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = blockIdx.x % a.n_seg;
@@ -349,6 +350,7 @@ state_partial_phi_bf16_kernel(StateArgs a) {
   const int64_t r1 = (r0 + a.seg_len < a.n) ? r0 + a.seg_len : a.n;
   const int nrows = (int)(r1 - r0);
   const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.phik) + ((int64_t)bh * a.phik_rows + r0) * F;
+  const float* zw = a.zw ? a.zw + (int64_t)bh * a.phik_rows + r0 : nullptr;
 
   RowSrc vs;
   {
@@ -407,6 +409,8 @@ state_partial_phi_bf16_kernel(StateArgs a) {
             (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
       }
     }
+    if (zw && tid < kTileRows)
+      zws[tid] = (ti * kTileRows + tid < nrows) ? zw[ti * kTileRows + tid] : 0.0f;
     if (ti + 1 < ntiles) load((int64_t)(ti + 1) * kTileRows);
     __syncthreads();
     if (a.vt_out) {
@@ -432,8 +436,15 @@ state_partial_phi_bf16_kernel(StateArgs a) {
         for (int j = 0; j < 2; ++j) {
           const bf16x8 af = frag_tr(pt, PLD, 32 * kb + 16 * j, 32 * fb, lane);
           const u32x4 au = as_u32x4(af);
+          if (zw) {
+            const int rb = 32 * kb + 16 * j + 8 * (lane >> 5);   // rows of this fragment
 #pragma unroll
-          for (int e = 0; e < 4; ++e) zp[p] += bf16_lo(au[e]) + bf16_hi(au[e]);
+            for (int e = 0; e < 4; ++e)
+              zp[p] += bf16_lo(au[e]) * zws[rb + 2 * e] + bf16_hi(au[e]) * zws[rb + 2 * e + 1];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zp[p] += bf16_lo(au[e]) + bf16_hi(au[e]);
+          }
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
             const int d = 32 * db + (lane & 31);

@@ -10,7 +10,8 @@ from typing import Optional
 
 import torch
 
-from . import (BF16, BIDIR, CAUSAL, F32, PHI_ELU, PHI_MLP, PHI_POLY2, Desc, rehyat_hybrid_fwd,
+from . import (BF16, BIDIR, CAUSAL, F32, PHI_ELU, PHI_MLP, PHI_POLY2, Desc, rehyat_hybrid_bwd,
+               rehyat_hybrid_bwd_workspace, rehyat_hybrid_fwd, rehyat_hybrid_fwd_stats,
                rehyat_hybrid_fwd_workspace, rehyat_phi, rehyat_recurrent_step,
                rehyat_recurrent_step_workspace, rehyat_state_update,
                rehyat_state_update_workspace)
@@ -91,6 +92,35 @@ def hybrid_fwd(q, k, v, Wq, Wk=None, *, HW: int, Tc: int, To: int, causal: bool 
         ws = workspace(rehyat_hybrid_fwd_workspace(d), q.device)
     rehyat_hybrid_fwd(d, q, k, v, Wq, Wk, y, ws)
     return y
+
+
+def hybrid_fwd_stats(q, k, v, Wq, Wk=None, *, HW: int, Tc: int, To: int, causal: bool = True,
+                     y_dtype: torch.dtype = torch.float32):
+    """(y, lse): the whole-sequence forward and log2 of each row's joint normaliser."""
+    Wk = Wq if Wk is None else Wk
+    N = q.shape[2]
+    d = make_desc(q, Wq, T=N // HW, HW=HW, Tc=Tc, To=To, causal=causal, y_dtype=y_dtype)
+    y = torch.empty(q.shape, dtype=y_dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws = workspace(rehyat_hybrid_fwd_workspace(d), q.device)
+    rehyat_hybrid_fwd_stats(d, q, k, v, Wq, Wk, y, lse, ws)
+    return y, lse
+
+
+def hybrid_bwd(q, k, v, Wq, Wk, y, lse, dy, *, HW: int, Tc: int, To: int):
+    """Gradients of sum(dy * y) of the causal form: dict of dq, dk, dv (fp32 [B,H,N,D]) and
+    dWq, dWk (fp32, shaped like W)."""
+    Wk = Wq if Wk is None else Wk
+    N = q.shape[2]
+    d = make_desc(q, Wq, T=N // HW, HW=HW, Tc=Tc, To=To, causal=True, y_dtype=y.dtype)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(q.shape, **f32),
+           "dv": torch.empty(q.shape, **f32), "dWq": torch.empty(Wq.shape, **f32),
+           "dWk": torch.empty(Wk.shape, **f32)}
+    ws = workspace(rehyat_hybrid_bwd_workspace(d), q.device)
+    rehyat_hybrid_bwd(d, q, k, v, Wq, Wk, y, lse, dy, out["dq"], out["dk"], out["dv"], out["dWq"],
+                      out["dWk"], ws)
+    return out
 
 
 def phi(x, W, fmap: Optional[FeatureMap] = None) -> torch.Tensor:

@@ -136,6 +136,16 @@ rehyat_status rehyat_hybrid_fwd(const rehyat_desc* desc, const void* q, const vo
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * rehyat_hybrid_fwd that also writes, for every query row, the log2 of its joint
+ * normaliser (key design 1): lse[b,h,i] = log2(n^S_i + n^L_i), the softmax weights taken
+ * as exp(q.k/sqrt(D)) without any stabiliser. The backward (rehyat_hybrid_bwd) takes it.
+ *   lse [B, H, N] fp32 (device, written); other arguments as for rehyat_hybrid_fwd.
+ */
+rehyat_status rehyat_hybrid_fwd_stats(const rehyat_desc* desc, const void* q, const void* k,
+                                      const void* v, const void* Wq, const void* Wk, void* y,
+                                      float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One chunk of the causal form run as the chunk-wise RNN (key design 4), the sampling-time
  * use in which one chunk of Tc frames is produced at a time with the state carried.
  *   chunk_index t >= 0; the chunk holds frames [t*Tc, min((t+1)*Tc, T)), c_f of them.
@@ -158,6 +168,31 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* desc, int32_t chunk_index
                                     const void* Wq, const void* Wk, float* S, float* z,
                                     void* k_tail, void* v_tail, void* y_c,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the non-recursive causal form (key designs 1 and 4: the form the method is
+ * trained and its feature maps distilled with): the gradients of sum(dy * y) for
+ * y = rehyat_hybrid_fwd(q, k, v, Wq, Wk), the fixed feature map.
+ *   q, k, v [B, H, N, D] bf16, Wq, Wk as for the forward (device)
+ *   y    [B, H, N, D] y_dtype: the forward's output (device)
+ *   lse  [B, H, N] fp32: from rehyat_hybrid_fwd_stats (device)
+ *   dy   [B, H, N, D] y_dtype (device)
+ *   dq, dk, dv [B, H, N, D] fp32 (device, written)
+ *   dWq, dWk   [D, F] or [H, D, F] fp32 (device, written): summed over the batch (and over
+ *              the heads for a shared W). When Wq and Wk are one tensor, its gradient is
+ *              dWq + dWk.
+ *   ws   device scratch of at least rehyat_hybrid_bwd_workspace(desc) bytes.
+ * Supported: dtype bf16 (D = 128, F in {64, 128, 256}), phi_kind REHYAT_PHI_POLY2, mode
+ * REHYAT_CAUSAL; other descriptors return REHYAT_ERR_UNSUPPORTED. The window products run
+ * on bf16 MFMA with fp32 accumulation; dy, dy/den, the softmax weights and their gradients,
+ * phi and the feature gradients are rounded to bf16 where they enter an MFMA.
+ */
+size_t rehyat_hybrid_bwd_workspace(const rehyat_desc* desc);
+rehyat_status rehyat_hybrid_bwd(const rehyat_desc* desc, const void* q, const void* k,
+                                const void* v, const void* Wq, const void* Wk, const void* y,
+                                const float* lse, const void* dy, float* dq, float* dk,
+                                float* dv, float* dWq, float* dWk, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* rehyat_status_str(rehyat_status status);

@@ -41,7 +41,7 @@ import torch
 
 __all__ = [
     "HybridConfig", "CONFIGS", "config", "make_inputs", "make_custom", "to_f64", "TORCH_DTYPE",
-    "make_mlp_map_params",
+    "make_mlp_map_params", "make_upstream",
 ]
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -163,6 +163,13 @@ def make_mlp_map_params(D: int, hidden: int, F: int, *, seed: int, P: int = 2,
     b2 = torch.tensor(np.repeat(np.asarray(psi_mean, dtype=np.float64), F // P),
                       dtype=torch.float32).expand(lead + (F,)).clone()
     return {n: t.to(torch.bfloat16) for n, t in (("W1", W1), ("b1", b1), ("W2", W2), ("b2", b2))}
+
+
+def make_upstream(shape, *, seed: int, dtype: str) -> torch.Tensor:
+    """Seeded upstream gradient dy ~ N(0, 1) of the given shape, rounded to `dtype`
+    (generator seeded with seed + 7919, drawn after nothing else)."""
+    g = torch.Generator().manual_seed(int(seed) + 7919)
+    return torch.randn(tuple(shape), generator=g).to(TORCH_DTYPE[dtype])
 
 
 def make_inputs(cfg: HybridConfig) -> Dict[str, torch.Tensor]:

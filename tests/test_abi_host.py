@@ -201,3 +201,46 @@ def test_feature_map_workspace_sizes():
             BH * d.Tc * E * 4 + gather + BH * img + (30 + 40) * rows)
         assert L.rehyat_state_update_workspace(ctypes.byref(d.c()), 1000) == (
             BH * 2 * E * 4 + 1000 * rows)
+
+
+def bwd(desc, **kw):
+    L = hs.lib()
+    names = ("q", "k", "v", "Wq", "Wk", "y", "lse", "dy", "dq", "dk", "dv", "dWq", "dWk", "ws")
+    ptrs = {n: P[i] for i, n in enumerate(names)}
+    ptrs.update(kw)
+    need = L.rehyat_hybrid_bwd_workspace(ctypes.byref(desc.c()))
+    ws_bytes = kw.pop("ws_bytes", need) if "ws_bytes" in kw else need
+    return L.rehyat_hybrid_bwd(ctypes.byref(desc.c()), *[ptrs[n] for n in names], ws_bytes, None)
+
+
+def test_backward_validation():
+    d = _desc()
+    assert bwd(_desc(mode=hs.BIDIR)) == ERR_UNSUP
+    assert bwd(_desc(dtype=hs.F32, D=64)) == ERR_UNSUP
+    assert bwd(_desc(phi_kind=hs.PHI_ELU)) == ERR_UNSUP
+    assert bwd(d, lse=None) == ERR_NULL
+    assert bwd(d, dWk=None) == ERR_NULL
+    assert bwd(d, dq=P[0] + 8) == ERR_ALIGN
+    assert bwd(d, ws_bytes=16) == ERR_WS
+    assert bwd(d, dq=P[0]) == ERR_ALIAS              # dq over q
+    assert bwd(d, dv=P[8] + 64) == ERR_ALIAS         # dv inside dq
+    L = hs.lib()
+    # stats forward: lse required, not overlapping y
+    need = L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c()))
+    assert L.rehyat_hybrid_fwd_stats(ctypes.byref(d.c()), P[0], P[1], P[2], P[3], P[4], P[5], None,
+                                     P[6], need, None) == ERR_NULL
+    assert L.rehyat_hybrid_fwd_stats(ctypes.byref(d.c()), P[0], P[1], P[2], P[3], P[4], P[5],
+                                     P[5] + 16, P[6], need, None) == ERR_ALIAS
+
+
+def test_backward_workspace_size():
+    L = hs.lib()
+    d = _desc()
+    BH, N, T, E, F = d.B * d.H, d.T * d.HW, d.T, d.F * d.D + d.F, d.F
+    r = lambda n: (n + 255) // 256 * 256
+    expect = sum(r(x) for x in (BH * T * E * 4, BH * d.n_chunks * E * 4, BH * T * E * 4,
+                                BH * d.n_chunks * F * d.D * 2, BH * T * F * d.D * 2, F * d.D * 2,
+                                F * d.D * 2, BH * N * d.D * 2, BH * N * d.D * 2, BH * N * 4,
+                                BH * N * 4, BH * N * F * 2, BH * N * F * 2, BH * N * F * 2,
+                                BH * F * d.D * 4, BH * F * 4))
+    assert L.rehyat_hybrid_bwd_workspace(ctypes.byref(d.c())) == expect
