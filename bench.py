@@ -20,6 +20,7 @@ whole sequence) with librehyat and with torch's SDPA.
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-context]
     python bench.py --phi mlp|elu   the same line with another feature map of key design 3
     python bench.py --sweep     (Tc, To) grid of the ablation, one JSON line per entry
+    python bench.py --bwd       the backward of the causal form on the same workload
 """
 from __future__ import annotations
 
@@ -85,6 +86,100 @@ def flop_model(B, H, T, HW, D, F, Tc, To, causal=True, phi_row_flop=None):
     state = pf * keys_state + 2 * F * D * keys_state
     BH = B * H
     return BH * (attn + state), BH * attn, BH * state, pairs
+
+
+def flop_model_bwd(B, H, T, HW, D, F, Tc, To):
+    """Algorithmic FLOPs of the causal backward (fixed map).
+
+    window pairs: 10*D each (the scores again, dP = dy.v, and the dq, dk, dv products);
+    query rows with a linear set: 10*D*F (phi(q), S g, W gq, dWq, and the reverse state
+    phi(q) g^T); keys in some linear set: 12*D*F (phi(k), the forward state phi(k)^T v,
+    G v, G^T phi(k), W gk, dWk). Returns (total, dk/dv-kernel part, dq-kernel part).
+    """
+    N, Np = T * HW, Tc * HW
+    pairs = rows_lin = 0
+    t = 0
+    while t * Np < N:
+        r0, r1 = t * Np, min((t + 1) * Np, N)
+        lo = max(t * Np - To * HW, 0)
+        pairs += (r1 - r0) * (r1 - lo)
+        rows_lin += (r1 - r0) if lo > 0 else 0
+        t += 1
+    keys_lin = max((t - 1) * Np - To * HW, 0)
+    BH = B * H
+    total = BH * (10 * D * pairs + 10 * D * F * rows_lin + 12 * D * F * keys_lin)
+    dkdv = BH * (8 * D * pairs + 8 * D * F * keys_lin)     # as the dk/dv kernel runs them
+    dq = BH * (6 * D * pairs + 6 * D * F * rows_lin)       # as the dq kernel runs them
+    return total, dkdv, dq
+
+
+def bench_bwd(args):
+    """One line for the backward: rehyat_hybrid_bwd at 21x30x52 (y, lse resident)."""
+    import torch
+    import synthetic as syn
+    import hybrid_softmax_linear_amd as hs
+    from hybrid_softmax_linear_amd import torch_api as ta
+    cfg = syn.config(3)
+    inp = syn.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v, W = (inp[n].to(dev) for n in ("q", "k", "v", "W"))
+    dy = syn.make_upstream(tuple(q.shape), seed=cfg.seed, dtype="f32").to(dev)
+    desc = hs.Desc(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, F=cfg.F, Tc=cfg.Tc, To=cfg.To,
+                   dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL)
+    stream = torch.cuda.current_stream().cuda_stream
+    y = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    wsf = ta.workspace(hs.rehyat_hybrid_fwd_workspace(desc), dev)
+    hs.rehyat_hybrid_fwd_stats(desc, q, k, v, W, W, y, lse, wsf, stream=stream)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(q.shape, **f32) for _ in range(3))
+    dWq, dWk = torch.empty(W.shape, **f32), torch.empty(W.shape, **f32)
+    ws = ta.workspace(hs.rehyat_hybrid_bwd_workspace(desc), dev)
+
+    def step():
+        hs.rehyat_hybrid_bwd(desc, q, k, v, W, W, y, lse, dy, dq, dk, dv, dWq, dWk, ws,
+                             stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    times = {}
+    for kern, name in ((2, "dkdv"), (3, "dq")):
+        hs.rehyat_timing_enable(True, kern)
+        ms = time_calls(step, args.steps, 0)
+        kms, n = hs.rehyat_timing_read()
+        hs.rehyat_timing_enable(False)
+        times[name] = (kms / max(n, 1), n, ms)
+    ms = min(t[2] for t in times.values())
+    total, f_dkdv, f_dq = flop_model_bwd(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D, cfg.F, cfg.Tc, cfg.To)
+    dk_ms, dk_n, _ = times["dkdv"]
+    dq_ms, dq_n, _ = times["dq"]
+    fwd_ms = time_calls(lambda: hs.rehyat_hybrid_fwd_stats(desc, q, k, v, W, W, y, lse, wsf,
+                                                            stream=stream), max(3, args.steps // 2), 2)
+    tokens = cfg.B * cfg.N
+    result = {
+        "metric": "hybrid-attn backward tokens/s & TFLOP/s per MI355X at 21×30×52",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "21x30x52 latent (480x832, 5 s): B2 H12 D128 F128, Tc3 To1, causal, "
+                               "one rehyat_hybrid_bwd call per step (y, lse and dy resident)",
+                   "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)"},
+        "tflops": total / (ms * 1e-3) / 1e12,
+        "mfma_peak_frac": total / (ms * 1e-3) / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+        "flop_per_step": total,
+        "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel<128>",
+                     "achieved": f_dkdv / (dk_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": f_dkdv / (dk_ms * 1e-3) / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+                     "traffic": None, "flop_per_launch": f_dkdv, "avg_launch_ms": dk_ms,
+                     "launches_timed": dk_n},
+        "cpu_baseline": None,
+        "context": {"dq_kernel_ms": dq_ms, "dq_kernel_tflops": f_dq / (dq_ms * 1e-3) / 1e12,
+                    "fwd_stats_ms": fwd_ms, "fwd_plus_bwd_ms": fwd_ms + ms},
+    }
+    print(json.dumps(result))
+    return 0
 
 
 # ---- CPU baseline: the float64 oracle on a bounded sample --------------------------------
@@ -223,6 +318,9 @@ def main(argv=None):
                     help="instead of the default line: time every (Tc, To) of the pages' "
                          "ablation grid at the 21x30x52 and 21x20x30 latents next to full "
                          "softmax, one JSON line per configuration")
+    ap.add_argument("--bwd", action="store_true",
+                    help="instead of the default line: the backward of the causal form "
+                         "(rehyat_hybrid_bwd) on the same workload")
     ap.add_argument("--phi", choices=("poly2", "elu", "mlp"), default="poly2",
                     help="feature map of the timed step (default: the fixed map)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -242,6 +340,8 @@ def main(argv=None):
     hs.lib()   # fail loudly if the HIP library is missing
     if args.sweep:
         return sweep(args)
+    if args.bwd:
+        return bench_bwd(args)
     cfg = syn.config(3)
     inp = syn.make_inputs(cfg)
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)

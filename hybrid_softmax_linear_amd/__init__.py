@@ -228,8 +228,10 @@ def rehyat_recurrent_step(desc: Desc, chunk_index: int, q_c, k_c, v_c, Wq, Wk, S
            "rehyat_recurrent_step")
 
 
-def rehyat_timing_enable(enable: bool) -> None:
-    _check(lib().rehyat_timing_enable(1 if enable else 0), "rehyat_timing_enable")
+def rehyat_timing_enable(enable, kernel: int = 1) -> None:
+    """Time the launches of one kernel: 1 forward attention, 2 backward dk/dv, 3 backward
+    dq (enable=False disables)."""
+    _check(lib().rehyat_timing_enable(int(kernel) if enable else 0), "rehyat_timing_enable")
 
 
 def rehyat_timing_read() -> Tuple[float, int]:

@@ -172,18 +172,19 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 constexpr int kMaxTimed = 4096;
 struct Timing {
   bool enabled = false;
+  int which = 1;   // kernel whose launches are timed (rehyat_timing_enable's argument)
   bool created = false;
   int count = 0;
   hipEvent_t ev[2 * kMaxTimed];
 };
 Timing g_timing;
 
-void timed_begin(hipStream_t s) {
-  if (g_timing.enabled && g_timing.count < kMaxTimed)
+void timed_begin(hipStream_t s, int which = 1) {
+  if (g_timing.enabled && g_timing.which == which && g_timing.count < kMaxTimed)
     (void)hipEventRecord(g_timing.ev[2 * g_timing.count], s);
 }
-void timed_end(hipStream_t s) {
-  if (g_timing.enabled && g_timing.count < kMaxTimed) {
+void timed_end(hipStream_t s, int which = 1) {
+  if (g_timing.enabled && g_timing.which == which && g_timing.count < kMaxTimed) {
     (void)hipEventRecord(g_timing.ev[2 * g_timing.count + 1], s);
     g_timing.count++;
   }
@@ -777,7 +778,10 @@ rehyat_status rehyat_hybrid_bwd(const rehyat_desc* d, const void* q, const void*
     b.tiles_per_chunk = (int)((Np + 255) / 256);
     b.tiles_last = (last_rows + 255) / 256;
     b.tiles_per_head = (nch - 1) * b.tiles_per_chunk + b.tiles_last;
-    REHYAT_TRY(launch_bwd_dq(b, F, BH * b.tiles_per_head, s), "dq launch");
+    timed_begin(s, 3);
+    e = launch_bwd_dq(b, F, BH * b.tiles_per_head, s);
+    timed_end(s, 3);
+    if (e != hipSuccess) return hip_status(e, "dq launch");
   }
   // 4. reverse states: per query frame sums phi(q) g^T and phi(q) c, suffix over chunks
   {
@@ -799,7 +803,10 @@ rehyat_status rehyat_hybrid_bwd(const rehyat_desc* d, const void* q, const void*
     b.tiles_per_chunk = (int)((Np + 127) / 128);
     b.tiles_last = (last_rows + 127) / 128;
     b.tiles_per_head = (nch - 1) * b.tiles_per_chunk + b.tiles_last;
-    REHYAT_TRY(launch_bwd_dkdv(b, F, BH * b.tiles_per_head, s), "dk/dv launch");
+    timed_begin(s, 2);
+    e = launch_bwd_dkdv(b, F, BH * b.tiles_per_head, s);
+    timed_end(s, 2);
+    if (e != hipSuccess) return hip_status(e, "dk/dv launch");
   }
   // 6. dW = sum over rows of x gx^T (per frame, folded per head, summed over heads / batch)
   for (int side = 0; side < 2; ++side) {
@@ -826,7 +833,9 @@ rehyat_status rehyat_timing_enable(int32_t enable) {
     }
     g_timing.created = true;
   }
+  if (enable < 0 || enable > 3) return fail(REHYAT_ERR_SHAPE, "timing selector %d unknown", enable);
   g_timing.enabled = enable != 0;
+  g_timing.which = enable;
   g_timing.count = 0;
   return ok();
 }

@@ -201,11 +201,13 @@ const char* rehyat_status_str(rehyat_status status);
 const char* rehyat_last_error(void);
 
 /*
- * Kernel timing (measurement aid). While enabled, every launch of the hybrid-attention
- * kernel is bracketed by HIP events recorded on the launch stream (events are created
- * once, at most 4096 launches are recorded). rehyat_timing_read synchronises on the last
- * recorded event and returns the summed kernel time in milliseconds and the launch count,
- * then clears the record. Enabling clears the record too. Not thread-safe.
+ * Kernel timing (measurement aid). While enabled, every launch of one kernel is bracketed
+ * by HIP events recorded on the launch stream (events are created once, at most 4096
+ * launches are recorded). The argument selects it: 1 the hybrid-attention kernel of the
+ * forward, 2 the dk/dv kernel and 3 the dq kernel of rehyat_hybrid_bwd; 0 disables.
+ * rehyat_timing_read synchronises on the last recorded event and returns the summed kernel
+ * time in milliseconds and the launch count, then clears the record. Enabling clears the
+ * record too. Not thread-safe.
  */
 rehyat_status rehyat_timing_enable(int32_t enable);
 rehyat_status rehyat_timing_read(double* total_ms, int64_t* launches);
