@@ -201,7 +201,7 @@ dw_finalize_kernel(const float* __restrict__ parts, int64_t E, int BH, int H, in
 constexpr int kQW = 8;                                   // waves of the dq kernel
 constexpr int kLinLds = 3 * 128 * kRowB;                 // W^T, S and W slabs
 constexpr int kKeyTile = 64;
-constexpr int kDqLds = kLinLds > 2 * kKeyTile * kRowB ? kLinLds : 2 * kKeyTile * kRowB;
+constexpr int kDqLds = kLinLds > 4 * kKeyTile * kRowB ? kLinLds : 4 * kKeyTile * kRowB;
 
 struct BwdGeo {
   int bh, t;
@@ -353,22 +353,30 @@ bwd_dq_kernel(BwdArgs a) {
   const int nk = (int)(g.hi - g.lo);
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (hrow + g.lo) * kDim;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + (hrow + g.lo) * kDim;
-  unsigned char* sK = smem;
-  unsigned char* sV = smem + kKeyTile * kRowB;
+  unsigned char* sK = smem;                      // buffer b: K tile at sK + b * 2 * kKeyTile * kRowB
+  unsigned char* sV = smem + kKeyTile * kRowB;   //           V tile right after it
   const int ab = kappa(lane & 31) * kRowB + 16 * (lane >> 5);
   const float ls = a.logit_scale;
-#pragma unroll 1
-  for (int k0 = 0; k0 < nk; k0 += kKeyTile) {
-    __syncthreads();
+  auto issue = [&](int k0, int buf) {
     const int bytes = (nk - k0) * 256;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * kDim), (short)0, bytes, kBufWord3);
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * kDim), (short)0, bytes, kBufWord3);
-    dma_rows<kKeyTile, kQW>(kr, sK, wave, lane);
-    dma_rows<kKeyTile, kQW>(vr, sV, wave, lane);
+    dma_rows<kKeyTile, kQW>(kr, sK + buf * 2 * kKeyTile * kRowB, wave, lane);
+    dma_rows<kKeyTile, kQW>(vr, sV + buf * 2 * kKeyTile * kRowB, wave, lane);
+  };
+  __syncthreads();   // the linear part's slabs are no longer read
+  issue(0, 0);
+  int buf = 0;
+#pragma unroll 1
+  for (int k0 = 0; k0 < nk; k0 += kKeyTile) {
     wait_vmem_all();
-    __syncthreads();
+    __syncthreads();   // this tile landed everywhere; the other buffer is free
+    if (k0 + kKeyTile < nk) issue(k0 + kKeyTile, buf ^ 1);
+    const unsigned char* bK = sK + buf * 2 * kKeyTile * kRowB;
+    const unsigned char* bV = sV + buf * 2 * kKeyTile * kRowB;
+    buf ^= 1;
     if (!active) continue;
 #pragma unroll 1
     for (int kb = 0; kb < kKeyTile / 32; ++kb) {
@@ -378,8 +386,8 @@ bwd_dq_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) St[i] = Pt[i] = 0.0f;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        St = mfma32(as_bf16x8(lds_read16(sK, ab + kb * 32 * kRowB + 32 * s)), Qf[s], St);
-        Pt = mfma32(as_bf16x8(lds_read16(sV, ab + kb * 32 * kRowB + 32 * s)), DYf[s], Pt);
+        St = mfma32(as_bf16x8(lds_read16(bK, ab + kb * 32 * kRowB + 32 * s)), Qf[s], St);
+        Pt = mfma32(as_bf16x8(lds_read16(bV, ab + kb * 32 * kRowB + 32 * s)), DYf[s], Pt);
       }
       bf16x8 dsb[2];
 #pragma unroll
@@ -403,7 +411,7 @@ bwd_dq_kernel(BwdArgs a) {
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          dQ[db] = mfma32(frag_tr(sK, kRowB, 32 * kb + 16 * j, 32 * db, lane), dsb[j], dQ[db]);
+          dQ[db] = mfma32(frag_tr(bK, kRowB, 32 * kb + 16 * j, 32 * db, lane), dsb[j], dQ[db]);
     }
   }
   if (ok) {
