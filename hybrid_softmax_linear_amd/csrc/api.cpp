@@ -27,8 +27,7 @@ hipError_t launch_fold_states(const float* part, int nseg, float* S, float* z, i
                               int init, int BH, hipStream_t stream);
 hipError_t launch_gather_window_bf16(const void* ka, const void* va, int64_t a_rows, int64_t a_row0,
                                      const void* kb, const void* vb, int64_t b_rows, int64_t na,
-                                     int64_t nk, int nwin, int Tc_rows, int To_rows, int max_rows,
-                                     void* vt_out, int64_t vt_ld, void* k_out, int64_t k_ld, int BH,
+                                     int64_t nk, void* k_out, void* v_out, int64_t ld, int BH,
                                      hipStream_t stream);
 hipError_t launch_copy_rows(const void* sk, const void* sv, void* dk, void* dv, int64_t src_rows,
                             int64_t src_row0, int64_t rows, int row_bytes, int BH,
@@ -218,25 +217,7 @@ constexpr int kStateSegRows = 512;   // rows per segment for rehyat_state_update
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// bf16 whole-sequence form: V^T is written by the state kernel when every frame boundary
-// is 8-aligned (16-byte rows of keys); otherwise each chunk's window is gathered.
-bool fwd_fused_vt(const rehyat_desc* d) { return d->HW % 8 == 0 && n_chunks(d) > 1; }
-
-int64_t fwd_window_ld(const rehyat_desc* d) {
-  const int64_t N = (int64_t)d->T * d->HW;
-  const int64_t w = (int64_t)(d->Tc + d->To) * d->HW;
-  return round_up(w < N ? w : N, 64);
-}
-
-size_t fwd_vt_bytes(const rehyat_desc* d) {
-  if (d->dtype != REHYAT_BF16) return 0;
-  const size_t BH = (size_t)d->B * d->H;
-  const int64_t N = (int64_t)d->T * d->HW;
-  if (fwd_fused_vt(d)) return BH * d->D * (size_t)N * 2;
-  return BH * (size_t)n_chunks(d) * d->D * (size_t)fwd_window_ld(d) * 2;
-}
-
-// streaming form: the window (tail + chunk) is gathered into K [nk_max][D] and V^T [D][ld]
+// streaming form (bf16): the window (tail + chunk) is gathered into K and V [nk_max][D]
 // bf16 path: images of the linear-branch operands in the attention kernel's LDS layout,
 // F*256 bytes per state (S^T) and per W (W^T).
 size_t image_bytes(const rehyat_desc* d) { return (size_t)d->F * 256; }
@@ -246,11 +227,9 @@ size_t w_images_bytes(const rehyat_desc* d) {
 }
 
 int64_t step_nk_max(const rehyat_desc* d) { return (int64_t)(d->Tc + d->To) * d->HW; }
-int64_t step_vt_ld(const rehyat_desc* d) { return round_up(step_nk_max(d), 64); }
 size_t step_gather_bytes(const rehyat_desc* d) {
   if (d->dtype != REHYAT_BF16) return 0;
-  const size_t BH = (size_t)d->B * d->H;
-  return BH * (size_t)step_nk_max(d) * d->D * 2 + BH * d->D * (size_t)step_vt_ld(d) * 2;
+  return 2 * (size_t)d->B * d->H * (size_t)step_nk_max(d) * d->D * 2;
 }
 
 rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k, const void* v,
@@ -387,8 +366,7 @@ size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* d) {
   // maps evaluated ahead: phi(k) and phi(q) rows of the whole sequence
   const size_t phis = (phi_ahead(d) && n_chunks(d) > 1)
                           ? 2 * phi_rows_bytes(d, (int64_t)d->T * d->HW) : 0;
-  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + fwd_vt_bytes(d) +
-         imgs + phis;
+  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + imgs + phis;
 }
 
 rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
@@ -443,15 +421,13 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
   const size_t E = state_elems(d);
   float* part = reinterpret_cast<float*>(ws);              // [BH][T][E]
   float* states = part + (size_t)BH * d->T * E;             // [BH][nch][E]
-  void* vt = states + (size_t)BH * nch * E;                  // V^T (bf16 path)
-  unsigned char* simg = reinterpret_cast<unsigned char*>(vt) + fwd_vt_bytes(d);   // S^T images
+  unsigned char* simg = reinterpret_cast<unsigned char*>(states + (size_t)BH * nch * E);   // S^T images
   unsigned char* wimg = simg + (size_t)BH * nch * image_bytes(d);                 // W^T images
   unsigned char* phik = wimg + w_images_bytes(d);            // phi rows (maps evaluated ahead)
   unsigned char* phiq = phik + phi_rows_bytes(d, N);
   const float us = 1.0f / std::sqrt((float)d->D);
   const bool need_state = nch > 1;   // a single chunk has an empty linear set in both modes
   const bool bf16 = d->dtype == REHYAT_BF16;
-  const bool fused_vt = bf16 && fwd_fused_vt(d);
 
   if (need_state) {
     StateArgs sa{};
@@ -463,8 +439,6 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
     sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
     sa.part = part;
     sa.u_scale = us;
-    sa.vt_out = fused_vt ? vt : nullptr;
-    sa.vt_ld = N;
     if (phi_ahead(d)) {
       hipError_t e = launch_phi_rows(d, k, N, Wk, phik, s);
       if (e == hipSuccess) e = launch_phi_rows(d, q, N, Wq, phiq, s);
@@ -488,19 +462,6 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
   a.q = q; a.q_rows = N; a.y = y;
   a.ka = k; a.va = v; a.a_rows = N;
   a.kb = k; a.vb = v; a.b_rows = N;
-  if (bf16) {
-    a.vt = vt;
-    if (fused_vt) {
-      a.vt_bh = (int64_t)d->D * N; a.vt_t = 0; a.vt_ld = N; a.vt_key0_is_lo = 1;
-    } else {
-      const int64_t ldw = fwd_window_ld(d);
-      hipError_t e = launch_gather_window_bf16(k, v, N, 0, k, v, N, N, N, nch, d->Tc * d->HW,
-                                               d->To * d->HW, 0, vt, ldw, nullptr, 0, BH, s);
-      if (e != hipSuccess) return hip_status(e, "window gather launch");
-      a.vt_bh = (int64_t)nch * d->D * ldw; a.vt_t = (int64_t)d->D * ldw; a.vt_ld = ldw;
-      a.vt_key0_is_lo = 0;
-    }
-  }
   a.Wq = Wq; a.w_per_head = d->w_per_head;
   a.S = states; a.z = states + (size_t)d->F * d->D;
   a.s_bh = (int64_t)nch * E; a.s_t = (int64_t)E; a.z_bh = a.s_bh; a.z_t = a.s_t;
@@ -589,10 +550,9 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
   void* phik_step = nullptr;   // phi rows of the gathered window keys
   void* kwin_step = nullptr;
   if (d->dtype == REHYAT_BF16) {
-    // gather the window contiguously: K [nk_max][D] and V^T [D][ld] per head
+    // gather the window contiguously: K and V [nk_max][D] per head
     uint16_t* kwin = reinterpret_cast<uint16_t*>(part + (size_t)BH * d->Tc * state_elems(d));
-    uint16_t* vtwin = kwin + (size_t)BH * step_nk_max(d) * d->D;
-    const int64_t ld = step_vt_ld(d);
+    uint16_t* vwin = kwin + (size_t)BH * step_nk_max(d) * d->D;
     // images of the carried state S^T and of W^T for the linear branch
     unsigned char* simg = reinterpret_cast<unsigned char*>(part + (size_t)BH * d->Tc * state_elems(d)) +
                           step_gather_bytes(d);
@@ -614,12 +574,11 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
     a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
     a.st_img = simg; a.st_img_bh = (int64_t)image_bytes(d); a.st_img_t = 0;
     hipError_t e = launch_gather_window_bf16(a.ka, a.va, a.a_rows, a.a_rows - tail_in, k_c, v_c,
-                                             crow, tail_in, tail_in + crow, 1, 0, 0, 0, vtwin, ld,
-                                             kwin, step_nk_max(d), BH, s);
+                                             crow, tail_in, tail_in + crow, kwin, vwin,
+                                             step_nk_max(d), BH, s);
     if (e != hipSuccess) return hip_status(e, "window gather launch");
-    a.ka = kwin; a.a_rows = step_nk_max(d);
+    a.ka = kwin; a.va = vwin; a.a_rows = step_nk_max(d);
     kwin_step = kwin;
-    a.vt = vtwin; a.vt_bh = (int64_t)d->D * ld; a.vt_t = 0; a.vt_ld = ld; a.vt_key0_is_lo = 0;
   }
   a.Wq = Wq; a.w_per_head = d->w_per_head;
   a.S = S; a.z = z;

@@ -10,10 +10,11 @@
 // hide each other's softmax and LDS latency behind their MFMAs. Work is done transposed:
 // S^T = K Q^T (A = K from LDS, B = Q^T held in registers), so each lane owns one query
 // column and the sums over keys stay inside the lane pair (l, l^32); the exponentiated
-// tile P^T feeds O^T = V^T P^T as the B operand without leaving registers. K tiles
-// ([128 keys][128 d]) and V^T tiles ([128 d][128 keys], from a V^T copy in HBM) stream into
-// LDS by buffer loads that write LDS directly (no staging registers); rows past the window
-// come back as zeros from the buffer descriptor's range check.
+// tile P^T feeds O^T = V^T P^T as the B operand without leaving registers. K and V tiles
+// ([128 keys][128 d], straight from the q/k/v layout) stream into LDS by buffer loads that
+// write LDS directly (no staging registers); rows past the window come back as zeros from
+// the buffer descriptor's range check. The V^T operand fragments come from the row-major V
+// tile by the transposing LDS read.
 //
 // The linear branch enters as one extra "key" of weight n^L and value a^L/n^L. All
 // exponentials of a query row share one fixed reference m0 (log2 units):
@@ -40,8 +41,13 @@ constexpr int kKeys = 128;                               // keys per LDS tile
 constexpr int kRow = 272;                                // LDS row: 256 B of data + 16 B pad
 constexpr int kDmaInsts = kKeys * (kRow / 16) / 64;      // 1 KB DMA instructions per tile (34)
 constexpr int kKBytes = kKeys * kRow;                    // K tile [128 keys][128 d] bf16
-constexpr int kVBytes = kKeys * kRow;                    // V^T tile [128 d][128 keys] bf16
-constexpr int kStageBytes = kKBytes + kVBytes;           // 68 KB per stage
+// V tiles are row-major too, rows padded to 288 B (72 words, 8 mod 64): the transposing
+// LDS read that forms the V^T fragments touches 4 rows x 32 bytes per 16 lanes, and that
+// stride keeps them on distinct banks.
+constexpr int kVRow = 288;                               // V row: 256 B + 32 B pad
+constexpr int kVInsts = kKeys * (kVRow / 16) / 64;       // 36
+constexpr int kVBytes = kKeys * kVRow;                   // V tile [128 keys][128 d] bf16
+constexpr int kStageBytes = kKBytes + kVBytes;           // 70 KB per stage
 constexpr int kBufRsrcWord3 = 0x00020000;                // gfx9 buffer descriptor word 3
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -65,24 +71,23 @@ struct Geo {
 // Tile sources of one workgroup: K rows of the window and the V^T rows of the window.
 struct Src {
   __amdgpu_buffer_rsrc_t k;     // base = first window row, range = nk rows
-  __amdgpu_buffer_rsrc_t vt;    // base = V^T of the head (or window), range = its extent
-  int vt_ld_bytes;              // bytes between V^T rows (d)
-  int vt_key0_bytes;            // byte offset of window key 0 inside a V^T row
+  __amdgpu_buffer_rsrc_t v;     // base = first window row of V, range = nk rows
   int nk;                       // window length
 };
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }   // vmcnt(0) lgkmcnt(0)
 
-// Tile layout in LDS (K tile and V^T tile alike): row r (a key for K, a d for V^T) of
-// 256 B at r * 272, its 16-byte chunk c at + 16 c. The 16-byte pad shifts consecutive rows
-// by four banks, so the 16 lanes of a read group (16 consecutive rows, one chunk) cover all
-// 64 banks, and every fragment read below is one per-lane base plus a constant offset.
+// Tile layout in LDS: K row r (a key) of 256 B at r * 272, its 16-byte chunk c at + 16 c.
+// The 16-byte pad shifts consecutive rows by four banks, so the 16 lanes of a read group
+// (16 consecutive rows, one chunk) cover all 64 banks, and every fragment read below is one
+// per-lane base plus a constant offset. V row r at r * 288 (see kVRow).
 
 // Issue the direct-to-LDS loads of tile kt into one stage. Each instruction writes 64
-// consecutive 16-byte slots (1 KB) of a tile; slot u holds row u / 17, chunk u % 17, and
-// the pad slot (chunk 16) takes a second copy of chunk 0. 34 instructions per tile, spread
-// over the 8 waves.
+// consecutive 16-byte slots (1 KB) of a tile; for K slot u holds row u / 17, chunk u % 17
+// (the pad slot, chunk 16, takes a second copy of chunk 0); for V row u / 18, chunk u % 18
+// (pad slots 16 and 17 copy chunk 0). 34 + 36 instructions per tile, spread over the 8
+// waves.
 __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* stage, int wave,
                                          int lane) {
 #pragma unroll
@@ -95,9 +100,18 @@ __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* st
       c = c == 16 ? 0 : c;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, (lds_void*)(stage + j * 1024), 16,
                                                (kt * kKeys + r) * 256 + c * 16, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          s.vt, (lds_void*)(stage + kKBytes + j * 1024), 16,
-          r * s.vt_ld_bytes + s.vt_key0_bytes + (kt * kKeys + 8 * c) * 2, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (kVInsts + NW - 1) / NW; ++i) {
+    const int j = wave + NW * i;
+    if (j < kVInsts) {
+      const int u = 64 * j + lane;
+      const int r = u / 18;
+      int c = u - 18 * r;
+      c = c >= 16 ? 0 : c;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.v, (lds_void*)(stage + kKBytes + j * 1024), 16,
+                                               (kt * kKeys + r) * 256 + c * 16, 0, 0, 0);
     }
   }
 }
@@ -112,16 +126,16 @@ __device__ __forceinline__ void load_k(bf16x8 (&kf)[8], const unsigned char* kbu
   for (int s = 0; s < 8; ++s) kf[s] = as_bf16x8(lds_read16(kbuf, base + kb * 32 * kRow + s * 32));
 }
 
-// V^T fragments (A operand of O^T += V^T P^T) of 32-key block kb: lane l takes d row
-// 32 db + l % 32 at key chunk 4 kb + 2 j + l / 32.
+// V^T fragments (A operand of O^T += V^T P^T) of 32-key block kb: lane l takes column
+// d = 32 db + l % 32 of the row-major V tile at keys 32 kb + 16 j + 8 (l / 32) .. + 7, by
+// the transposing LDS read.
 __device__ __forceinline__ void load_v(bf16x8 (&vf)[4][2], const unsigned char* vbuf, int kb,
                                        int lane) {
-  const int base = (lane & 31) * kRow + (lane >> 5) * 16;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      vf[db][j] = as_bf16x8(lds_read16(vbuf, base + db * 32 * kRow + kb * 64 + j * 32));
+      vf[db][j] = frag_tr(vbuf, kVRow, 32 * kb + 16 * j, 32 * db, lane);
 }
 
 // S^T block (32 keys x 32 queries) from K fragments.
@@ -485,7 +499,7 @@ template <int F>
 __global__ void __launch_bounds__(NT)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 hybrid_attn_bf16_kernel(AttnArgs a) {
-  // 136 KB: two K/V^T stages during the key loop; W^T and S^T slabs for the linear branch.
+  // 140 KB: two K/V stages during the key loop; W^T and S^T slabs for the linear branch.
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
   __shared__ float zs[F];
   __shared__ int bad_flag;
@@ -529,19 +543,16 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // ---- tile sources: K rows of the window, V^T of the window ---------------------------
+  // ---- tile sources: K and V rows of the window ---------------------------
   Src src;
   {
     const int nk = (int)(g.hi - g.lo);
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.ka) +
                             head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
     src.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nk * 256, kBufRsrcWord3);
-    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.vt) + g.bh * a.vt_bh +
-                            g.t_local * a.vt_t;
-    src.vt = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, (int)(kDim * a.vt_ld * 2),
-                                               kBufRsrcWord3);
-    src.vt_ld_bytes = (int)(a.vt_ld * 2);
-    src.vt_key0_bytes = (int)((a.vt_key0_is_lo ? g.lo : 0) * 2);
+    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.va) +
+                            head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
+    src.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nk * 256, kBufRsrcWord3);
     src.nk = nk;
   }
   const float ls = a.logit_scale;

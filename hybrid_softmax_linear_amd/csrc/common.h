@@ -124,10 +124,9 @@ struct AttnArgs {
   // head strides. For the whole-sequence form A is the sequence itself and nb = 0.
   const void* ka; const void* va; int64_t a_rows;
   const void* kb; const void* vb; int64_t b_rows;
-  // V^T of the window for the bf16 path: head bh, chunk t_local at
-  // vt + bh*vt_bh + t_local*vt_t, rows d of vt_ld elements; window key 0 sits at column
-  // lo of a row when vt_key0_is_lo (V^T of the whole sequence), else at column 0.
-  const void* vt; int64_t vt_bh, vt_t, vt_ld; int vt_key0_is_lo;
+  // The bf16 kernel reads K and V of the window from segment A alone: the whole sequence
+  // (window of chunk t at rows [lo, hi)) or, with step set, a gathered window (rows
+  // [0, hi - lo)), a_rows rows per head.
   const void* Wq;       // [D, F] or [H, D, F]
   int w_per_head;
   const float* S;       // linear state of (head, chunk): S + bh*s_bh + t*s_t, [F, D]
@@ -193,8 +192,6 @@ struct StateArgs {
   const void* Wk; int w_per_head; int H;
   float* part;          // [BH, n_seg, F*D + F] fp32 partial (S then z)
   float u_scale;
-  // optional (bf16 path): V^T of the virtual rows, [BH][D][vt_ld] bf16, column = row index
-  void* vt_out; int64_t vt_ld;
   // optional (bf16 path): phi(k) computed ahead, virtual row w of head bh at
   // phik + (bh * phik_rows + w) * F; NULL: phi(k) = 1 + u + u^2/2 from Wk in the kernel
   const void* phik; int64_t phik_rows;

@@ -78,20 +78,6 @@ state_partial_bf16_kernel(StateArgs a) {
     // the next tile's global loads fly while this tile is reduced
     if (ti + 1 < ntiles) tile_load(r, ks, vs, (int64_t)(ti + 1) * kTileRows, tid);
     __syncthreads();
-    if (a.vt_out) {
-      // V^T of these rows (needs seg_len and the row count multiples of 8): 128 d rows x
-      // 8 chunks of 8 keys, straight from the transposed LDS tile.
-      uint16_t* vo = reinterpret_cast<uint16_t*>(a.vt_out) + (int64_t)bh * kDim * a.vt_ld +
-                     r0 + ti * kTileRows;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int id = it * 256 + tid;
-        const int d = id >> 3, kc = id & 7;
-        if (ti * kTileRows + 8 * kc < nrows)
-          *reinterpret_cast<u32x4*>(vo + (int64_t)d * a.vt_ld + 8 * kc) =
-              *reinterpret_cast<const u32x4*>(vt + vtile_chunk_off(d, kc));
-      }
-    }
     if (!active) continue;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -217,65 +203,27 @@ phi_bf16_kernel(const uint16_t* x, int64_t n, const uint16_t* Wall, int w_per_he
   }
 }
 
-// Window gather for the bf16 attention kernel: window rows [0, nk) (rows [0, na) from
-// segment A, the rest from segment B) -> V^T [BH][nwin][128][vt_ld] (columns >= nk zeroed)
-// and, when k_out is set, K [BH][nwin][k_ld][128]. One workgroup per (head, window, 64
-// rows); window w of a sequence starts at row w_stride*w (w_stride = 0: one window).
+// Window gather for the bf16 attention kernel of the streaming step: window rows [0, nk)
+// (rows [0, na) from segment A starting at row a_row0, the rest from segment B) -> K and V
+// [BH][ld][128], rows >= nk left as they are (the kernel's range check stops at nk). One
+// thread per 16-byte chunk, 16 chunks per row.
 __global__ void __launch_bounds__(256)
 gather_window_bf16_kernel(const uint16_t* ka, const uint16_t* va, int64_t a_rows, int64_t a_row0,
                           const uint16_t* kb, const uint16_t* vb, int64_t b_rows, int64_t na,
-                          int64_t nk, int nwin, int64_t w_stride, int Tc_rows, int To_rows,
-                          uint16_t* vt_out, int64_t vt_ld, uint16_t* k_out, int64_t k_ld,
-                          int blocks_per_win) {
-  __shared__ uint16_t tile[64][136];
-  const int tid = threadIdx.x;
-  const int blk = blockIdx.x % blocks_per_win;
-  const int wbh = blockIdx.x / blocks_per_win;
-  const int w = wbh % nwin, bh = wbh / nwin;
-  // rows of window w (multi-window form: window w = [max(w*Tc_rows - To_rows, 0), ...))
-  int64_t wlo = 0, wn = nk;
-  if (nwin > 1 || w_stride > 0) {
-    wlo = (int64_t)w * Tc_rows - To_rows > 0 ? (int64_t)w * Tc_rows - To_rows : 0;
-    const int64_t whi = ((int64_t)w + 1) * Tc_rows < a_rows ? ((int64_t)w + 1) * Tc_rows : a_rows;
-    wn = whi - wlo;
-  }
-  const int64_t r0 = (int64_t)blk * 64;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int id = it * 256 + tid;
-    const int row = id >> 4, c = id & 15;
-    const int64_t wr = r0 + row;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
-    if (wr < wn) {
-      const int64_t g = wlo + wr;
-      const uint16_t* kp = (g < na) ? ka + head_off(bh, a_rows, kDim) + (a_row0 + g) * kDim
-                                    : kb + head_off(bh, b_rows, kDim) + (g - na) * kDim;
-      const uint16_t* vp = (g < na) ? va + head_off(bh, a_rows, kDim) + (a_row0 + g) * kDim
-                                    : vb + head_off(bh, b_rows, kDim) + (g - na) * kDim;
-      kv = *reinterpret_cast<const u32x4*>(kp + 8 * c);
-      vv = *reinterpret_cast<const u32x4*>(vp + 8 * c);
-      if (k_out)
-        *reinterpret_cast<u32x4*>(k_out + ((int64_t)wbh * k_ld + wr) * kDim + 8 * c) = kv;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[row][8 * c + 2 * e] = (uint16_t)(vv[e] & 0xffffu);
-      tile[row][8 * c + 2 * e + 1] = (uint16_t)(vv[e] >> 16);
-    }
-  }
-  __syncthreads();
-  uint16_t* vo = vt_out + (int64_t)wbh * kDim * vt_ld + r0;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int id = it * 256 + tid;
-    const int d = id >> 3, kc = id & 7;
-    if (r0 + 8 * kc >= vt_ld) continue;
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = (unsigned)tile[8 * kc + 2 * e][d] | ((unsigned)tile[8 * kc + 2 * e + 1][d] << 16);
-    *reinterpret_cast<u32x4*>(vo + (int64_t)d * vt_ld + 8 * kc) = o;
-  }
+                          int64_t nk, uint16_t* k_out, uint16_t* v_out, int64_t ld,
+                          int blocks_per_head) {
+  const int bh = blockIdx.x / blocks_per_head;
+  const int64_t id = (int64_t)(blockIdx.x % blocks_per_head) * 256 + threadIdx.x;
+  const int64_t w = id >> 4;
+  const int c = (int)(id & 15);
+  if (w >= nk) return;
+  const int64_t src = (w < na) ? head_off(bh, a_rows, kDim) + (a_row0 + w) * kDim
+                               : head_off(bh, b_rows, kDim) + (w - na) * kDim;
+  const uint16_t* kp = (w < na) ? ka : kb;
+  const uint16_t* vp = (w < na) ? va : vb;
+  const int64_t dst = ((int64_t)bh * ld + w) * kDim + 8 * c;
+  *reinterpret_cast<u32x4*>(k_out + dst) = *reinterpret_cast<const u32x4*>(kp + src + 8 * c);
+  *reinterpret_cast<u32x4*>(v_out + dst) = *reinterpret_cast<const u32x4*>(vp + src + 8 * c);
 }
 
 // bf16 images of the linear-branch operands of the attention kernel, laid out byte for
@@ -413,18 +361,6 @@ state_partial_phi_bf16_kernel(StateArgs a) {
       zws[tid] = (ti * kTileRows + tid < nrows) ? zw[ti * kTileRows + tid] : 0.0f;
     if (ti + 1 < ntiles) load((int64_t)(ti + 1) * kTileRows);
     __syncthreads();
-    if (a.vt_out) {
-      uint16_t* vo = reinterpret_cast<uint16_t*>(a.vt_out) + (int64_t)bh * kDim * a.vt_ld +
-                     r0 + ti * kTileRows;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int id = it * 256 + tid;
-        const int d = id >> 3, kc = id & 7;
-        if (ti * kTileRows + 8 * kc < nrows)
-          *reinterpret_cast<u32x4*>(vo + (int64_t)d * a.vt_ld + 8 * kc) =
-              *reinterpret_cast<const u32x4*>(vt + vtile_chunk_off(d, kc));
-      }
-    }
     if (!active) continue;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -708,16 +644,14 @@ phi_mlp_bf16_kernel(const uint16_t* __restrict__ x, int64_t n, const uint16_t* _
 
 hipError_t launch_gather_window_bf16(const void* ka, const void* va, int64_t a_rows, int64_t a_row0,
                                      const void* kb, const void* vb, int64_t b_rows, int64_t na,
-                                     int64_t nk, int nwin, int Tc_rows, int To_rows, int max_rows,
-                                     void* vt_out, int64_t vt_ld, void* k_out, int64_t k_ld, int BH,
+                                     int64_t nk, void* k_out, void* v_out, int64_t ld, int BH,
                                      hipStream_t stream) {
-  const int bpw = (int)((vt_ld + 63) / 64);
-  (void)max_rows;
-  dim3 grid(BH * nwin * bpw), block(256);
+  if (nk <= 0) return hipSuccess;
+  const int bph = (int)((nk * 16 + 255) / 256);
+  dim3 grid(BH * bph), block(256);
   hipLaunchKernelGGL(gather_window_bf16_kernel, grid, block, 0, stream, (const uint16_t*)ka,
                      (const uint16_t*)va, a_rows, a_row0, (const uint16_t*)kb, (const uint16_t*)vb,
-                     b_rows, na, nk, nwin, (int64_t)(nwin > 1 ? 1 : 0), Tc_rows, To_rows,
-                     (uint16_t*)vt_out, vt_ld, (uint16_t*)k_out, k_ld, bpw);
+                     b_rows, na, nk, (uint16_t*)k_out, (uint16_t*)v_out, ld, bph);
   return hipGetLastError();
 }
 

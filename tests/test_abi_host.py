@@ -101,11 +101,10 @@ def test_workspace_sizes():
     d = _desc()
     E = d.F * d.D + d.F
     BH = d.B * d.H
-    vt = BH * d.n_chunks * d.D * 64 * 2   # HW=10: gathered V^T windows of 40 keys, 64-padded
     img = d.F * 256                       # one bf16 S^T or W^T image (F rows of 128 d)
     assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == (
-        BH * (d.T + d.n_chunks) * E * 4 + vt + BH * d.n_chunks * img + img)
-    gather = BH * 40 * d.D * 2 + BH * d.D * 64 * 2
+        BH * (d.T + d.n_chunks) * E * 4 + BH * d.n_chunks * img + img)
+    gather = 2 * BH * 40 * d.D * 2        # gathered K and V windows of (Tc + To) HW = 40 rows
     assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == (
         BH * d.Tc * E * 4 + gather + BH * img + img)
     dh = _desc(w_per_head=1)              # one W^T image per head
@@ -188,14 +187,13 @@ def test_feature_map_workspace_sizes():
     E = base.F * base.D + base.F
     N = base.T * base.HW
     img = base.F * 256
-    vt = BH * base.n_chunks * base.D * 64 * 2
-    gather = BH * 40 * base.D * 2 + BH * base.D * 64 * 2
+    gather = 2 * BH * 40 * base.D * 2
     for kw in (dict(phi_kind=hs.PHI_ELU), dict(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=2)):
         d = _desc(**kw)
         rows = BH * d.F * 2                      # bytes of one bf16 phi row for every head
         # whole sequence: S^T images but no W^T image, phi(k) and phi(q) of all N rows
         assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == (
-            BH * (d.T + d.n_chunks) * E * 4 + vt + BH * d.n_chunks * img + 2 * N * rows)
+            BH * (d.T + d.n_chunks) * E * 4 + BH * d.n_chunks * img + 2 * N * rows)
         # one chunk: phi(q_c) of Tc*HW rows and phi of the (Tc + To)*HW window keys
         assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == (
             BH * d.Tc * E * 4 + gather + BH * img + (30 + 40) * rows)
