@@ -21,6 +21,8 @@ whole sequence) with librehyat and with torch's SDPA.
     python bench.py --phi mlp|elu   the same line with another feature map of key design 3
     python bench.py --sweep     (Tc, To) grid of the ablation, one JSON line per entry
     python bench.py --bwd       the backward of the causal form on the same workload
+    python bench.py --stream    the 81x30x52 streaming workload: 27 single-launch recurrent
+                                steps per pass (chunks resident in HBM)
 """
 from __future__ import annotations
 
@@ -182,6 +184,79 @@ def bench_bwd(args):
     return 0
 
 
+def bench_stream(args):
+    """One line for streaming: 27 recurrent steps over the 81x30x52 latent (B1 H12, Tc3 To1),
+    each step's q, k, v chunk resident in HBM; a pass is the 27 steps, each one launch of
+    rehyat_recurrent_step_fused. Context: the same pass with rehyat_recurrent_step (seven
+    launches per step)."""
+    import torch
+    import synthetic as syn
+    import hybrid_softmax_linear_amd as hs
+    from hybrid_softmax_linear_amd import torch_api as ta
+    cfg = syn.config(4)
+    inp = syn.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    Np = cfg.Tc * cfg.HW
+    W = inp["W"].to(dev)
+    chunks = [tuple(inp[n][:, :, t * Np:(t + 1) * Np].contiguous().to(dev) for n in ("q", "k", "v"))
+              for t in range(cfg.n_chunks)]
+    del inp
+    yc = torch.empty(chunks[0][0].shape, dtype=torch.float32, device=dev)
+    steps = cfg.n_chunks
+
+    def timed(fused, kernel):
+        rec = ta.Recurrent(cfg.B, cfg.H, cfg.D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
+                           device=dev, fused=fused)
+
+        def one_pass():
+            rec.t = 0
+            for (qc, kc, vc) in chunks:
+                rec.step(qc, kc, vc, W, out=yc)
+
+        for _ in range(args.warmup):
+            one_pass()
+        torch.cuda.synchronize()
+        hs.rehyat_timing_enable(True, kernel)
+        ms = time_calls(one_pass, args.steps, 0)
+        kms, n = hs.rehyat_timing_read()
+        hs.rehyat_timing_enable(False)
+        return ms, kms / max(n, 1), n
+
+    ms, step_ms, n = timed(True, 4)
+    ms_multi, attn_ms_multi, _ = timed(False, 1)
+    total, attn_total = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D, cfg.F, cfg.Tc, cfg.To)[:2]
+    per_launch = total / steps
+    result = {
+        "metric": "hybrid-attn streaming tokens/s per MI355X at 81×30×52",
+        "value": cfg.B * cfg.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "81x30x52 latent: B1 H12 D128 F128, Tc3 To1, causal, 27 "
+                               "rehyat_recurrent_step_fused calls per step (one pass over the "
+                               "video)",
+                   "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)"},
+        "tflops": total / (ms * 1e-3) / 1e12,
+        "mfma_peak_frac": total / (ms * 1e-3) / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+        "flop_per_step": total,
+        "roofline": {"bound": "mfma", "kernel": "recurrent_step_bf16_kernel<128>",
+                     "achieved": per_launch / (step_ms * 1e-3) / 1e12,
+                     "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": per_launch / (step_ms * 1e-3) / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+                     "traffic": None, "flop_per_launch": per_launch,
+                     "avg_launch_ms": step_ms, "launches_timed": n},
+        "cpu_baseline": None,
+        "context": {"ms_per_recurrent_step": ms / steps,
+                    "multi_launch_ms_per_pass": ms_multi,
+                    "multi_launch_ms_per_step": ms_multi / steps,
+                    "multi_launch_attention_kernel_ms": attn_ms_multi,
+                    "multi_launch_attention_tflops": attn_total / steps / (attn_ms_multi * 1e-3) / 1e12,
+                    "single_over_multi_launch_speedup": ms_multi / ms},
+    }
+    print(json.dumps(result))
+    return 0
+
+
 # ---- CPU baseline: the float64 oracle on a bounded sample --------------------------------
 
 def _oracle_head(args):
@@ -318,6 +393,8 @@ def main(argv=None):
                     help="instead of the default line: time every (Tc, To) of the pages' "
                          "ablation grid at the 21x30x52 and 21x20x30 latents next to full "
                          "softmax, one JSON line per configuration")
+    ap.add_argument("--stream", action="store_true",
+                    help="27 recurrent steps over the 81x30x52 latent per step")
     ap.add_argument("--bwd", action="store_true",
                     help="instead of the default line: the backward of the causal form "
                          "(rehyat_hybrid_bwd) on the same workload")
@@ -342,6 +419,8 @@ def main(argv=None):
         return sweep(args)
     if args.bwd:
         return bench_bwd(args)
+    if args.stream:
+        return bench_stream(args)
     cfg = syn.config(3)
     inp = syn.make_inputs(cfg)
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)

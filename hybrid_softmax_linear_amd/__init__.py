@@ -7,7 +7,7 @@ a call fails, an exception is raised.
 
 The functions carry the names of the C entry points (include/rehyat.h):
     rehyat_phi, rehyat_state_update, rehyat_hybrid_fwd, rehyat_hybrid_fwd_stats,
-    rehyat_hybrid_bwd, rehyat_recurrent_step
+    rehyat_hybrid_bwd, rehyat_recurrent_step, rehyat_recurrent_step_fused
 plus *_workspace helpers, rehyat_timing_enable / rehyat_timing_read.
 """
 from __future__ import annotations
@@ -22,6 +22,7 @@ __all__ = [
     "rehyat_phi", "rehyat_state_update", "rehyat_state_update_workspace",
     "rehyat_hybrid_fwd", "rehyat_hybrid_fwd_workspace",
     "rehyat_recurrent_step", "rehyat_recurrent_step_workspace",
+    "rehyat_recurrent_step_fused", "rehyat_recurrent_step_fused_workspace",
     "rehyat_hybrid_fwd_stats", "rehyat_hybrid_bwd", "rehyat_hybrid_bwd_workspace",
     "rehyat_timing_enable", "rehyat_timing_read", "F32", "BF16", "CAUSAL", "BIDIR",
     "PHI_POLY2", "PHI_ELU", "PHI_MLP",
@@ -97,8 +98,11 @@ _SIGS = {
     "rehyat_hybrid_fwd": (ctypes.c_int, [ctypes.POINTER(_CDesc)] + [ctypes.c_void_p] * 7 +
                           [ctypes.c_size_t, ctypes.c_void_p]),
     "rehyat_recurrent_step_workspace": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
+    "rehyat_recurrent_step_fused_workspace": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
     "rehyat_recurrent_step": (ctypes.c_int, [ctypes.POINTER(_CDesc), ctypes.c_int32] +
                               [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "rehyat_recurrent_step_fused": (ctypes.c_int, [ctypes.POINTER(_CDesc), ctypes.c_int32] +
+                                    [ctypes.c_void_p] * 13 + [ctypes.c_size_t, ctypes.c_void_p]),
     "rehyat_hybrid_fwd_stats": (ctypes.c_int, [ctypes.POINTER(_CDesc)] + [ctypes.c_void_p] * 8 +
                                 [ctypes.c_size_t, ctypes.c_void_p]),
     "rehyat_hybrid_bwd_workspace": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
@@ -228,9 +232,28 @@ def rehyat_recurrent_step(desc: Desc, chunk_index: int, q_c, k_c, v_c, Wq, Wk, S
            "rehyat_recurrent_step")
 
 
+def rehyat_recurrent_step_fused_workspace(desc: Desc) -> int:
+    return int(lib().rehyat_recurrent_step_fused_workspace(ctypes.byref(desc.c())))
+
+
+def rehyat_recurrent_step_fused(desc: Desc, chunk_index: int, q_c, k_c, v_c, Wq, Wk, S, z,
+                                k_tail, v_tail, k_tail_out, v_tail_out, y_c, ws,
+                                ws_bytes: Optional[int] = None, stream=None) -> None:
+    """One chunk of the chunk-wise RNN form in a single launch (see include/rehyat.h): the
+    tail is read from k_tail, v_tail and the new one written to k_tail_out, v_tail_out; ws
+    must be zeroed once before its first use."""
+    nb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(lib().rehyat_recurrent_step_fused(ctypes.byref(desc.c()), int(chunk_index), _ptr(q_c),
+                                             _ptr(k_c), _ptr(v_c), _ptr(Wq), _ptr(Wk), _ptr(S),
+                                             _ptr(z), _ptr(k_tail), _ptr(v_tail),
+                                             _ptr(k_tail_out), _ptr(v_tail_out), _ptr(y_c),
+                                             _ptr(ws), nb, _stream(stream)),
+           "rehyat_recurrent_step_fused")
+
+
 def rehyat_timing_enable(enable, kernel: int = 1) -> None:
-    """Time the launches of one kernel: 1 forward attention, 2 backward dk/dv, 3 backward
-    dq (enable=False disables)."""
+    """Time the launches of one kernel: 1 attention (forward and step), 2 backward dk/dv,
+    3 backward dq, 4 the single-launch step (enable=False disables)."""
     _check(lib().rehyat_timing_enable(int(kernel) if enable else 0), "rehyat_timing_enable")
 
 

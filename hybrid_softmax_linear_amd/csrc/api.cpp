@@ -12,6 +12,7 @@
 
 namespace rehyat {
 hipError_t launch_attn_bf16(const AttnArgs& a, int F, hipStream_t stream);
+hipError_t launch_step_bf16(const AttnArgs& a, const StepArgs& s, int F, hipStream_t stream);
 int attn_bf16_tile_rows();
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int F, hipStream_t stream);
 int attn_f32_tile_rows();
@@ -480,7 +481,54 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
   return hip_status(launch_attention(d, a, s), "attention launch");
 }
 
+// frames in chunk t
+int step_frames(const rehyat_desc* d, int32_t t) {
+  return (d->T - t * d->Tc) < d->Tc ? (d->T - t * d->Tc) : d->Tc;
+}
+
+// Argument checks of the recurrent step (both forms); need = the workspace size.
+rehyat_status check_step(const rehyat_desc* d, int32_t t, const void* q_c, const void* k_c,
+                         const void* v_c, const void* Wq, const void* Wk, const float* S,
+                         const float* z, const void* k_tail, const void* v_tail, const void* y_c,
+                         const void* ws, size_t ws_bytes, size_t need) {
+  if (d->To > d->Tc) return fail(REHYAT_ERR_UNSUPPORTED, "recurrent step needs To <= Tc");
+  const int nch = n_chunks(d);
+  if (t < 0 || t >= nch) return fail(REHYAT_ERR_SHAPE, "chunk_index %d outside [0, %d)", t, nch);
+  const int cf = step_frames(d, t);
+  if (cf < d->To) return fail(REHYAT_ERR_UNSUPPORTED, "final chunk of %d frames is shorter than To = %d", cf, d->To);
+  if (!q_c || !k_c || !v_c || (needs_w(d) && (!Wq || !Wk)) || !S || !z || !y_c)
+    return fail(REHYAT_ERR_NULL, "q_c, k_c, v_c, Wq, Wk, S, z, y_c must be non-NULL");
+  if (d->To > 0 && (!k_tail || !v_tail)) return fail(REHYAT_ERR_NULL, "k_tail, v_tail needed when To > 0");
+  if (!aligned16(q_c) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(Wq) || !aligned16(Wk) ||
+      !aligned16(S) || !aligned16(z) || !aligned16(y_c) ||
+      (d->To > 0 && (!aligned16(k_tail) || !aligned16(v_tail))))
+    return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+  if (!ws || ws_bytes < need)
+    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (!aligned16(ws)) return fail(REHYAT_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const int BH = d->B * d->H;
+  const int64_t crow = (int64_t)cf * d->HW;          // rows in this chunk
+  const int64_t trow = (int64_t)d->To * d->HW;       // rows in the tail
+  const size_t es = esize(d->dtype);
+  const size_t nc = (size_t)BH * crow * d->D * es, nt = (size_t)BH * trow * d->D * es;
+  const size_t ny = (size_t)BH * crow * d->D * esize(d->y_dtype);
+  const size_t nS = (size_t)BH * d->F * d->D * 4, nz = (size_t)BH * d->F * 4;
+  const void* ins[3] = {q_c, k_c, v_c};
+  for (const void* p : ins) {
+    if (overlaps(y_c, ny, p, nc) || overlaps(S, nS, p, nc) || overlaps(z, nz, p, nc) ||
+        overlaps(k_tail, nt, p, nc) || overlaps(v_tail, nt, p, nc) || overlaps(ws, need, p, nc))
+      return fail(REHYAT_ERR_ALIAS, "outputs must not overlap the chunk inputs");
+  }
+  if (overlaps(S, nS, z, nz) || overlaps(y_c, ny, S, nS) || overlaps(y_c, ny, z, nz) ||
+      overlaps(k_tail, nt, v_tail, nt) || overlaps(y_c, ny, k_tail, nt) ||
+      overlaps(y_c, ny, v_tail, nt) || overlaps(ws, need, S, nS) || overlaps(ws, need, z, nz) ||
+      overlaps(ws, need, y_c, ny) || overlaps(ws, need, k_tail, nt) || overlaps(ws, need, v_tail, nt))
+    return fail(REHYAT_ERR_ALIAS, "outputs and workspace must not overlap");
+  return ok();
+}
+
 }  // namespace
+
 
 extern "C" {
 
@@ -502,39 +550,14 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
                                     void* y_c, void* ws, size_t ws_bytes, void* stream) {
   rehyat_status st = check_desc(d);
   if (st != REHYAT_OK) return st;
-  if (d->To > d->Tc) return fail(REHYAT_ERR_UNSUPPORTED, "recurrent step needs To <= Tc");
-  const int nch = n_chunks(d);
-  if (t < 0 || t >= nch) return fail(REHYAT_ERR_SHAPE, "chunk_index %d outside [0, %d)", t, nch);
-  const int cf = (d->T - t * d->Tc) < d->Tc ? (d->T - t * d->Tc) : d->Tc;   // frames in chunk
-  if (cf < d->To) return fail(REHYAT_ERR_UNSUPPORTED, "final chunk of %d frames is shorter than To = %d", cf, d->To);
-  if (!q_c || !k_c || !v_c || (needs_w(d) && (!Wq || !Wk)) || !S || !z || !y_c)
-    return fail(REHYAT_ERR_NULL, "q_c, k_c, v_c, Wq, Wk, S, z, y_c must be non-NULL");
-  if (d->To > 0 && (!k_tail || !v_tail)) return fail(REHYAT_ERR_NULL, "k_tail, v_tail needed when To > 0");
-  if (!aligned16(q_c) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(Wq) || !aligned16(Wk) ||
-      !aligned16(S) || !aligned16(z) || !aligned16(y_c) ||
-      (d->To > 0 && (!aligned16(k_tail) || !aligned16(v_tail))))
-    return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
   const size_t need = rehyat_recurrent_step_workspace(d);
-  if (!ws || ws_bytes < need)
-    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  st = check_step(d, t, q_c, k_c, v_c, Wq, Wk, S, z, k_tail, v_tail, y_c, ws, ws_bytes, need);
+  if (st != REHYAT_OK) return st;
   const int BH = d->B * d->H;
+  const int cf = step_frames(d, t);
   const int64_t crow = (int64_t)cf * d->HW;          // rows in this chunk
   const int64_t trow = (int64_t)d->To * d->HW;       // rows in the tail
   const size_t es = esize(d->dtype);
-  const size_t nc = (size_t)BH * crow * d->D * es, nt = (size_t)BH * trow * d->D * es;
-  const size_t ny = (size_t)BH * crow * d->D * esize(d->y_dtype);
-  const size_t nS = (size_t)BH * d->F * d->D * 4, nz = (size_t)BH * d->F * 4;
-  const void* ins[3] = {q_c, k_c, v_c};
-  for (const void* p : ins) {
-    if (overlaps(y_c, ny, p, nc) || overlaps(S, nS, p, nc) || overlaps(z, nz, p, nc) ||
-        overlaps(k_tail, nt, p, nc) || overlaps(v_tail, nt, p, nc) || overlaps(ws, need, p, nc))
-      return fail(REHYAT_ERR_ALIAS, "outputs must not overlap the chunk inputs");
-  }
-  if (overlaps(S, nS, z, nz) || overlaps(y_c, ny, S, nS) || overlaps(y_c, ny, z, nz) ||
-      overlaps(k_tail, nt, v_tail, nt) || overlaps(y_c, ny, k_tail, nt) ||
-      overlaps(y_c, ny, v_tail, nt) || overlaps(ws, need, S, nS) || overlaps(ws, need, z, nz) ||
-      overlaps(ws, need, y_c, ny) || overlaps(ws, need, k_tail, nt) || overlaps(ws, need, v_tail, nt))
-    return fail(REHYAT_ERR_ALIAS, "outputs and workspace must not overlap");
 
   hipStream_t s = (hipStream_t)stream;
   const float us = 1.0f / std::sqrt((float)d->D);
@@ -627,6 +650,96 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
     if (e != hipSuccess) return hip_status(e, "tail copy launch");
   }
   return ok();
+}
+
+size_t rehyat_recurrent_step_fused_workspace(const rehyat_desc* d) {
+  if (check_desc(d) != REHYAT_OK) return 0;
+  const size_t BH = (size_t)d->B * d->H;
+  // completion counters, then the new state and two frames' partials per head
+  return round_up((int64_t)(BH * sizeof(unsigned)), 256) + 3 * BH * state_elems(d) * sizeof(float);
+}
+
+rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* d, int32_t t, const void* q_c,
+                                          const void* k_c, const void* v_c, const void* Wq,
+                                          const void* Wk, float* S, float* z, const void* k_tail,
+                                          const void* v_tail, void* k_tail_out, void* v_tail_out,
+                                          void* y_c, void* ws, size_t ws_bytes, void* stream) {
+  rehyat_status st = check_desc(d);
+  if (st != REHYAT_OK) return st;
+  if (d->dtype != REHYAT_BF16 || d->phi_kind != REHYAT_PHI_POLY2)
+    return fail(REHYAT_ERR_UNSUPPORTED,
+                "the single-launch step supports bf16 inputs with the fixed feature map");
+  const size_t need = rehyat_recurrent_step_fused_workspace(d);
+  st = check_step(d, t, q_c, k_c, v_c, Wq, Wk, S, z, k_tail, v_tail, y_c, ws, ws_bytes, need);
+  if (st != REHYAT_OK) return st;
+  const int BH = d->B * d->H;
+  const int64_t crow = (int64_t)step_frames(d, t) * d->HW;   // rows in this chunk
+  const int64_t trow = (int64_t)d->To * d->HW;               // rows in the tail
+  const int64_t tail_in = (t > 0) ? trow : 0;                // tail rows in the window
+  if (d->To > 0) {
+    // the new tail: its own buffers, apart from everything else the call touches
+    if (!k_tail_out || !v_tail_out)
+      return fail(REHYAT_ERR_NULL, "k_tail_out, v_tail_out needed when To > 0");
+    if (!aligned16(k_tail_out) || !aligned16(v_tail_out))
+      return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const size_t es = esize(d->dtype);
+    const size_t nt = (size_t)BH * trow * d->D * es, nc = (size_t)BH * crow * d->D * es;
+    const size_t ny = (size_t)BH * crow * d->D * esize(d->y_dtype);
+    const size_t nS = (size_t)BH * d->F * d->D * 4, nz = (size_t)BH * d->F * 4;
+    const void* other[9] = {q_c, k_c, v_c, k_tail, v_tail, y_c, S, z, ws};
+    const size_t other_n[9] = {nc, nc, nc, nt, nt, ny, nS, nz, need};
+    for (void* o : {k_tail_out, v_tail_out})
+      for (int i = 0; i < 9; ++i)
+        if (overlaps(o, nt, other[i], other_n[i]))
+          return fail(REHYAT_ERR_ALIAS, "k_tail_out, v_tail_out must not overlap the other buffers");
+    if (overlaps(k_tail_out, nt, v_tail_out, nt))
+      return fail(REHYAT_ERR_ALIAS, "k_tail_out and v_tail_out must not overlap");
+  }
+  const size_t E = state_elems(d);
+  unsigned* counter = reinterpret_cast<unsigned*>(ws);
+  float* xs = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) +
+                                       round_up((int64_t)(BH * sizeof(unsigned)), 256));
+  const float us = 1.0f / std::sqrt((float)d->D);
+
+  AttnArgs a{};
+  a.q = q_c; a.q_rows = crow; a.y = y_c;
+  a.ka = k_tail ? k_tail : k_c; a.va = v_tail ? v_tail : v_c; a.a_rows = k_tail ? trow : crow;
+  a.kb = k_c; a.vb = v_c; a.b_rows = crow;
+  a.Wq = Wq; a.w_per_head = d->w_per_head;
+  a.S = S; a.z = z;
+  a.s_bh = (int64_t)d->F * d->D; a.s_t = 0; a.z_bh = d->F; a.z_t = 0;
+  a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
+  a.n_chunks = 1; a.chunk0 = t; a.step = 1; a.bidir = 0;
+  a.y_f32 = d->y_dtype == REHYAT_F32;
+  fill_tiles(a, d, 1, (int)crow);
+  a.logit_scale = kLog2e / std::sqrt((float)d->D);
+  a.u_scale = us;
+
+  StepArgs sp{};
+  // the window rows that no later window reaches (all but the last To frames), per frame
+  const int64_t nfold = tail_in + crow - trow;
+  StateArgs& sa = sp.fold;
+  sa.ka = a.ka; sa.va = a.va; sa.a_rows = a.a_rows; sa.a_row0 = 0;
+  sa.kb = k_c; sa.vb = v_c; sa.b_rows = crow; sa.b_row0 = 0;
+  sa.na = tail_in; sa.n = nfold;
+  sa.seg_len = d->HW;
+  sa.n_seg = (int)((nfold + d->HW - 1) / d->HW);
+  sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
+  sa.u_scale = us;
+  sp.fold_blocks = (int)round_up(BH, 8);
+  sp.per_head = a.tiles_per_head + 1;
+  sp.counter = counter;
+  sp.xs = xs;
+  sp.pp = xs + (size_t)BH * E;
+  sp.S = S; sp.z = z;
+  sp.init = t == 0;
+  sp.kc = k_c; sp.vc = v_c; sp.crow = crow;
+  sp.ktail = k_tail_out; sp.vtail = v_tail_out; sp.trow = d->To > 0 ? trow : 0;
+  hipStream_t s = (hipStream_t)stream;
+  timed_begin(s, 4);
+  const hipError_t e = launch_step_bf16(a, sp, d->F, s);
+  timed_end(s, 4);
+  return hip_status(e, "step launch");
 }
 
 size_t rehyat_hybrid_bwd_workspace(const rehyat_desc* d) {
@@ -792,7 +905,7 @@ rehyat_status rehyat_timing_enable(int32_t enable) {
     }
     g_timing.created = true;
   }
-  if (enable < 0 || enable > 3) return fail(REHYAT_ERR_SHAPE, "timing selector %d unknown", enable);
+  if (enable < 0 || enable > 4) return fail(REHYAT_ERR_SHAPE, "timing selector %d unknown", enable);
   g_timing.enabled = enable != 0;
   g_timing.which = enable;
   g_timing.count = 0;

@@ -26,7 +26,7 @@
 // first block may exceed m0; that is harmless while O and l stay finite (fp32 and bf16
 // share an 8-bit exponent). If any accumulator of the workgroup ends non-finite, the
 // workgroup recomputes with m0 = the exact row maximum over the window (all p <= 1).
-#include "tiles_bf16.h"
+#include "partial_bf16.h"
 
 namespace rehyat {
 
@@ -68,11 +68,17 @@ struct Geo {
   bool has_linear;
 };
 
-// Tile sources of one workgroup: K rows of the window and the V^T rows of the window.
+// Tile sources of one workgroup: K and V rows of the window. The streaming step's window
+// is in two segments (the carried tail, then the chunk): window rows [0, na) come from
+// k / v, the rest from k2 / v2, whose base sits na rows before the chunk's first row so
+// that one byte offset (window row * 256 + column) addresses either segment.
 struct Src {
-  __amdgpu_buffer_rsrc_t k;     // base = first window row, range = nk rows
-  __amdgpu_buffer_rsrc_t v;     // base = first window row of V, range = nk rows
+  __amdgpu_buffer_rsrc_t k;     // base = first window row, range = nk rows (na rows: step)
+  __amdgpu_buffer_rsrc_t v;
+  __amdgpu_buffer_rsrc_t k2;    // step: base = chunk row 0 - na rows, range = nk rows
+  __amdgpu_buffer_rsrc_t v2;
   int nk;                       // window length
+  int na_bytes;                 // step: 256 x the window rows in the first segment
 };
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
@@ -87,9 +93,12 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // consecutive 16-byte slots (1 KB) of a tile; for K slot u holds row u / 17, chunk u % 17
 // (the pad slot, chunk 16, takes a second copy of chunk 0); for V row u / 18, chunk u % 18
 // (pad slots 16 and 17 copy chunk 0). 34 + 36 instructions per tile, spread over the 8
-// waves.
-__device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* stage, int wave,
-                                         int lane) {
+// waves. kSplit: a lane whose byte offset lies past na_bytes loads from (k2, v2) instead
+// (the two loads of an instruction that straddles the boundary write disjoint lanes' slots).
+template <bool kSplit>
+__device__ __forceinline__ void tile_dma_from(__amdgpu_buffer_rsrc_t k, __amdgpu_buffer_rsrc_t v,
+                                              const Src& s, int kt, unsigned char* stage,
+                                              int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < (kDmaInsts + NW - 1) / NW; ++i) {
     const int j = wave + NW * i;
@@ -98,8 +107,12 @@ __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* st
       const int r = u / 17;
       int c = u - 17 * r;
       c = c == 16 ? 0 : c;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, (lds_void*)(stage + j * 1024), 16,
-                                               (kt * kKeys + r) * 256 + c * 16, 0, 0, 0);
+      const int off = (kt * kKeys + r) * 256 + c * 16;
+      if (!kSplit || off < s.na_bytes)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k, (lds_void*)(stage + j * 1024), 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k2, (lds_void*)(stage + j * 1024), 16, off, 0,
+                                                 0, 0);
     }
   }
 #pragma unroll
@@ -110,9 +123,34 @@ __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* st
       const int r = u / 18;
       int c = u - 18 * r;
       c = c >= 16 ? 0 : c;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.v, (lds_void*)(stage + kKBytes + j * 1024), 16,
-                                               (kt * kKeys + r) * 256 + c * 16, 0, 0, 0);
+      const int off = (kt * kKeys + r) * 256 + c * 16;
+      if (!kSplit || off < s.na_bytes)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v, (lds_void*)(stage + kKBytes + j * 1024), 16,
+                                                 off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.v2, (lds_void*)(stage + kKBytes + j * 1024),
+                                                 16, off, 0, 0, 0);
     }
+  }
+}
+
+// kTwo: the window is in two segments. A tile wholly inside one of them takes that
+// segment's descriptors (a uniform choice); only the tile that straddles the boundary
+// chooses per lane.
+template <bool kTwo>
+__device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* stage, int wave,
+                                         int lane) {
+  if (!kTwo) {
+    tile_dma_from<false>(s.k, s.v, s, kt, stage, wave, lane);
+    return;
+  }
+  const int t0 = kt * kKeys * 256;
+  if (t0 < s.na_bytes && t0 + kKeys * 256 > s.na_bytes) {
+    tile_dma_from<true>(s.k, s.v, s, kt, stage, wave, lane);
+  } else if (t0 < s.na_bytes) {
+    tile_dma_from<false>(s.k, s.v, s, kt, stage, wave, lane);
+  } else {
+    tile_dma_from<false>(s.k2, s.v2, s, kt, stage, wave, lane);
   }
 }
 
@@ -199,12 +237,57 @@ __device__ __forceinline__ void pv_mfma(Acc& A, const bf16x8 (&vf)[4][2], const 
     for (int db = 0; db < 4; ++db) A.O[db] = mfma32(vf[db][j], P[j], A.O[db]);
 }
 
+// Raw-operand staging (streaming step, where S is the caller's fp32 state): W slab
+// [128 d][FS] row-major at kWRow-byte rows, the 4-feature blocks of each 16 in the order
+// kappa (positions 4..7 and 8..11 swapped), so that the transposing read of physical
+// column 32 fb + (l mod 32) hands lane l the W^T row 32 fb + kappa(l mod 32) of the image
+// layout; bytes of the W slab, then the S^T slab.
+constexpr int kWRow = 288;
+constexpr int kWRawBytes = kDim * kWRow;
+
+// W[d][f0 .. f0+FS) of a [128][F] bf16 W into the raw W slab.
+template <int F, int FS>
+__device__ __forceinline__ void stage_w_raw(unsigned char* wt, const uint16_t* W, int f0, int tid) {
+#pragma unroll
+  for (int it = 0; it < (kDim * FS / 8 + NT - 1) / NT; ++it) {
+    const int id = it * NT + tid;
+    if (id < kDim * FS / 8) {
+      const int d = id / (FS / 8), c = id % (FS / 8);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)d * F + f0 + 8 * c);
+      const int col = 16 * (c >> 1) + ((c & 1) ? 4 : 0);   // logical block 2(c&1) -> kappa
+      unsigned char* row = wt + d * kWRow;
+      *reinterpret_cast<uint2*>(row + col * 2) = uint2{w[0], w[1]};
+      *reinterpret_cast<uint2*>(row + (col + 8) * 2) = uint2{w[2], w[3]};
+    }
+  }
+}
+
+// S[f0 .. f0+FS)[0 .. 128) (fp32) into the S^T slab: rows d of FS bf16, feature chunk c at
+// chunk c ^ (d mod FS/8), the layout (and rounding) of the S^T image.
+template <int FS>
+__device__ __forceinline__ void stage_st_raw(unsigned char* st, const float* S, int f0, int tid) {
+  constexpr int NCH = FS / 8;
+#pragma unroll
+  for (int it = 0; it < (kDim * NCH + NT - 1) / NT; ++it) {
+    const int id = it * NT + tid;
+    if (id < kDim * NCH) {
+      const int d = id & (kDim - 1), c = id >> 7;
+      const float* src = S + (int64_t)(f0 + 8 * c) * kDim + d;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16_u32(src[(2 * e) * kDim], src[(2 * e + 1) * kDim]);
+      *reinterpret_cast<u32x4*>(st + d * (FS * 2) + ((c ^ (d & (NCH - 1))) << 4)) = w;
+    }
+  }
+}
+
 // Linear branch: O = a^L^T = S^T phi(Q)^T (bf16 MFMA) and n^L = phi(q).z (full sum over
 // the lane pair). The W^T and S^T slabs of FS features come from bf16 images already in
 // the LDS layout (W^T rows f at chunk c ^ kappa(f & 15); S^T rows d at chunk
-// c ^ (d mod FS/8)) and are copied into `stage` (64 KB) by direct-to-LDS loads. Ends with a
-// barrier.
-template <int F>
+// c ^ (d mod FS/8)) and are copied into `stage` (64 KB) by direct-to-LDS loads; with kRaw
+// they are staged from W and the fp32 state through registers (same operand values, so
+// the same bits). Ends with a barrier.
+template <int F, bool kRaw>
 __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs& a,
                                               const Geo& g, const QRegs& Q, unsigned char* stage,
                                               float* zs, int tid, int lane, const uint16_t* pqrow) {
@@ -224,24 +307,32 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
       __builtin_amdgcn_make_buffer_rsrc((void*)wimg, (short)0, F * 256, kBufRsrcWord3);
   const __amdgpu_buffer_rsrc_t sr =
       __builtin_amdgcn_make_buffer_rsrc((void*)simg, (short)0, F * 256, kBufRsrcWord3);
-  unsigned char* wt = stage;              // [FS][128] bf16
-  unsigned char* st = stage + 32768;      // [128 d][FS] bf16
+  unsigned char* wt = stage;                               // [FS][128] bf16 (raw: [128][FS])
+  unsigned char* st = stage + (kRaw ? kWRawBytes : 32768);  // [128 d][FS] bf16
+  const uint16_t* wraw = reinterpret_cast<const uint16_t*>(a.Wq) +
+                         (a.w_per_head ? (int64_t)g.h * kDim * F : 0);
+  const float* sraw = a.S + g.bh * a.s_bh + g.t_local * a.s_t;
 #pragma unroll 1
   for (int f0 = 0; f0 < F; f0 += FS) {
     if (f0 > 0) __syncthreads();
-    const int base = (f0 / FS) * SLAB;
+    if (kRaw) {
+      if (!a.phiq) stage_w_raw<F, FS>(wt, wraw, f0, tid);
+      stage_st_raw<FS>(st, sraw, f0, tid);
+    } else {
+      const int base = (f0 / FS) * SLAB;
 #pragma unroll
-    for (int i = 0; i < (SLAB / 1024 + NW - 1) / NW; ++i) {
-      const int j = wave + NW * i;
-      if (j < SLAB / 1024) {
-        if (!a.phiq)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wt + j * 1024), 16,
+      for (int i = 0; i < (SLAB / 1024 + NW - 1) / NW; ++i) {
+        const int j = wave + NW * i;
+        if (j < SLAB / 1024) {
+          if (!a.phiq)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wt + j * 1024), 16,
+                                                     base + j * 1024 + lane * 16, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(st + j * 1024), 16,
                                                    base + j * 1024 + lane * 16, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(st + j * 1024), 16,
-                                                 base + j * 1024 + lane * 16, 0, 0, 0);
+        }
       }
+      wait_vmem();
     }
-    wait_vmem();
     __syncthreads();
     // U^T blocks: rows = features 32fb + kappa(l%32) (A = W^T), cols = queries (B = Q^T);
     // G chains at a time (fewer for F = 256, whose slab loop keeps more state live).
@@ -273,8 +364,13 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
       for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-          const int arow = 32 * (fg + k) + kappa(lane & 31);
-          bf16x8 av = as_bf16x8(lds_read16(wt, ktile_off(arow, 2 * s + (lane >> 5))));
+          bf16x8 av;
+          if (kRaw) {
+            av = frag_tr(wt, kWRow, 16 * s, 32 * (fg + k), lane);
+          } else {
+            const int arow = 32 * (fg + k) + kappa(lane & 31);
+            av = as_bf16x8(lds_read16(wt, ktile_off(arow, 2 * s + (lane >> 5))));
+          }
           U[k] = mfma32(av, Q.op[s], U[k]);
         }
       // phi = 1 + u + u^2/2, rounded to bf16: B operand of a^L^T = S^T phi^T.
@@ -385,6 +481,7 @@ __device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned ch
 }
 
 // Exact row maximum over the window (log2 units), for the overflow fallback.
+template <bool kTwo>
 __device__ __forceinline__ float max_sweep(const Src& src, const QRegs& Q, unsigned char* smem,
                                            float ls, int wave, int lane) {
   const int ntiles = (src.nk + kKeys - 1) / kKeys;
@@ -392,7 +489,7 @@ __device__ __forceinline__ float max_sweep(const Src& src, const QRegs& Q, unsig
 #pragma unroll 1
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();
-    tile_dma(src, kt, smem, wave, lane);
+    tile_dma<kTwo>(src, kt, smem, wave, lane);
     wait_vmem();
     __syncthreads();
 #pragma unroll
@@ -411,6 +508,7 @@ __device__ __forceinline__ float max_sweep(const Src& src, const QRegs& Q, unsig
 // direct-to-LDS tiles, one barrier per tile, the last tile peeled (masking).
 // Waves without a query tile (in workgroups that hold 7 of the chunk's wave tiles) only
 // help with the tile loads and barriers.
+template <bool kTwo>
 __device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const QRegs& Q,
                                          unsigned char* smem, float ls, int wave, int lane,
                                          bool active) {
@@ -425,7 +523,7 @@ __device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const
   for (int kt = 0; kt < ntiles - 1; ++kt) {
     unsigned char* cur = smem + (kt & 1) * kStageBytes;
     unsigned char* nxt = smem + ((kt & 1) ^ 1) * kStageBytes;
-    tile_dma(src, kt + 1, nxt, wave, lane);
+    tile_dma<kTwo>(src, kt + 1, nxt, wave, lane);
     if (active) {
       process_tile<false>(A, m0, cur, nxt, kt, nk, Q, ls, lane, kf, vf);
     } else {
@@ -495,21 +593,19 @@ __device__ __forceinline__ void tile_of_block(const AttnArgs& a, int b, int& bh,
   }
 }
 
-template <int F>
-__global__ void __launch_bounds__(NT)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-hybrid_attn_bf16_kernel(AttnArgs a) {
-  // 140 KB: two K/V stages during the key loop; W^T and S^T slabs for the linear branch.
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
-  __shared__ float zs[F];
-  __shared__ int bad_flag;
-
+// One attention workgroup: query tile `b` of the launch (in tile_of_block's order). smem:
+// 140 KB, two K/V stages during the key loop, W^T and S^T slabs for the linear branch.
+// kTwo: the window in two segments (the streaming step's carried tail, then the chunk);
+// kRaw: the linear operands staged from W and the fp32 state. Returns the head.
+template <int F, bool kTwo, bool kRaw>
+__device__ __forceinline__ int attention_block(const AttnArgs& a, int b, unsigned char* smem,
+                                               float* zs, int& bad_flag) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   Geo g;
   int qt;
-  tile_of_block(a, blockIdx.x, g.bh, g.t_local, qt);
+  tile_of_block(a, b, g.bh, g.t_local, qt);
   const int t = a.chunk0 + g.t_local;
   g.h = g.bh % a.H;
   const int64_t Np = (int64_t)a.Tc * a.HW;
@@ -547,20 +643,41 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
   Src src;
   {
     const int nk = (int)(g.hi - g.lo);
-    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.ka) +
-                            head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
-    src.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nk * 256, kBufRsrcWord3);
-    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.va) +
-                            head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
-    src.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nk * 256, kBufRsrcWord3);
     src.nk = nk;
+    if (kTwo) {
+      // rows [0, na): the last na rows of the tail (segment A); then the chunk (segment B),
+      // addressed from na rows before its start (no access below the chunk: a lane takes
+      // segment B only for offsets >= na * 256)
+      const int na = (int)(c0 - g.lo);
+      src.na_bytes = na * 256;
+      const int64_t ah = head_off(g.bh, a.a_rows, kDim) + (a.a_rows - na) * kDim;
+      const int64_t bh0 = head_off(g.bh, a.b_rows, kDim) - (int64_t)na * kDim;
+      src.k = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const uint16_t*>(a.ka) + ah), (short)0, na * 256, kBufRsrcWord3);
+      src.v = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const uint16_t*>(a.va) + ah), (short)0, na * 256, kBufRsrcWord3);
+      src.k2 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const uint16_t*>(a.kb) + bh0), (short)0, nk * 256, kBufRsrcWord3);
+      src.v2 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const uint16_t*>(a.vb) + bh0), (short)0, nk * 256, kBufRsrcWord3);
+    } else {
+      src.na_bytes = nk * 256;
+      const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.ka) +
+                              head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
+      src.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nk * 256, kBufRsrcWord3);
+      const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.va) +
+                              head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
+      src.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nk * 256, kBufRsrcWord3);
+      src.k2 = src.k;
+      src.v2 = src.v;
+    }
   }
   const float ls = a.logit_scale;
 
   // ---- linear branch, reference m0, key loop ------------------------------------------
   // Window tile 0 streams into stage 0 while the linear branch stages its operands in
   // stage 1.
-  tile_dma(src, 0, smem, wave, lane);
+  tile_dma<kTwo>(src, 0, smem, wave, lane);
   Acc A;
   float nl = 1.0f, ml = kNegBig;
   zero_acc(A);
@@ -570,12 +687,12 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
                 ((int64_t)g.bh * a.q_rows + g.q_row_base + qrow) * F
           : nullptr;
   if (g.has_linear) {
-    linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane, pqrow);
+    linear_branch<F, kRaw>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane, pqrow);
     ml = fast_log2(fabsf(nl));
   }
   float m0 = start_window(ml, src, Q, smem, ls, wave, lane);
   if (g.has_linear) scale_linear(A, nl, m0, lane);
-  key_loop(A, m0, src, Q, smem, ls, wave, lane, active);
+  key_loop<kTwo>(A, m0, src, Q, smem, ls, wave, lane, active);
 
   // ---- overflow guard: recompute the workgroup with the exact row maxima ---------------
   {
@@ -587,15 +704,16 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
     if (wave_any(bad) && lane == 0) atomicOr(&bad_flag, 1);
     __syncthreads();
     if (bad_flag) {
-      const float mx = max_sweep(src, Q, smem, ls, wave, lane);
+      const float mx = max_sweep<kTwo>(src, Q, smem, ls, wave, lane);
       zero_acc(A);
-      tile_dma(src, 0, smem, wave, lane);
-      if (g.has_linear) linear_branch<F>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane, pqrow);
+      tile_dma<kTwo>(src, 0, smem, wave, lane);
+      if (g.has_linear)
+        linear_branch<F, kRaw>(A, nl, a, g, Q, smem + kStageBytes, zs, tid, lane, pqrow);
       // reference = the exact maximum over the linear weight and every window key: every
       // p <= 1 and l >= 1
       m0 = start_window(fmaxf(ml, mx), src, Q, smem, ls, wave, lane);
       if (g.has_linear) scale_linear(A, nl, m0, lane);
-      key_loop(A, m0, src, Q, smem, ls, wave, lane, active);
+      key_loop<kTwo>(A, m0, src, Q, smem, ls, wave, lane, active);
     }
   }
 
@@ -624,11 +742,187 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
       }
     }
   }
+  return g.bh;
+}
+
+template <int F>
+__global__ void __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+hybrid_attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  __shared__ float zs[F];
+  __shared__ int bad_flag;
+  attention_block<F, false, false>(a, blockIdx.x, smem, zs, bad_flag);
+}
+
+// ---- single-launch recurrent step ------------------------------------------------------
+// One launch does the whole step of the chunk-wise RNN (papernotes.org ReHyAt note, key
+// design 4): the attention workgroups of the chunk (window = carried tail + chunk, linear
+// branch from the carried S, z), one fold workgroup per head and, in the last workgroup of
+// each head to finish, the update of S and z.
+//   * The fold workgroup forms the per-frame partial sums of the window rows that no later
+//     window reaches, two frames at a time (one per half of the workgroup, the state
+//     kernel's own arithmetic), and adds them onto S, z in frame order, exactly as the fold
+//     kernel does, into a workspace copy xs. It also writes the chunk's last To frames to
+//     the new tail, a buffer apart from the carried one.
+//   * Every workgroup of a head reports to the head's counter (a device-scope atomic) once
+//     its reads of S, z and the carried tail have returned; the one that completes the
+//     count is the only one left that could read S and z, and copies xs into them.
+// No workgroup waits for another. The only data that crosses workgroups inside the launch
+// is xs: the fold workgroup writes it with device-scope stores (through the XCD's L2) and
+// waits for them before it reports; the last workgroup reads it with device-scope loads.
+// (A full fence, an L2 write-back and invalidate of the XCD, in every workgroup cost more
+// than the whole fold.)
+
+// The fold workgroup of head bh: xs = ((S + p_0) + p_1) + ... over the nseg frames (S taken
+// as 0 for the first chunk), then the new tail. Each round the two halves form two frames'
+// partials and store them (pp: [2][F*D + F]); then all threads add them on elementwise.
+template <int F>
+__device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned char* smem, int tid) {
+  constexpr int E = F * kDim + F;
+  const int nseg = s.fold.n_seg;
+  const int half = tid >> 8, htid = tid & 255;
+  float* xs = s.xs + (int64_t)bh * E;
+  float* pp = s.pp + (int64_t)bh * 2 * E;
+  const float* S0 = s.S + (int64_t)bh * F * kDim;
+  const float* z0 = s.z + (int64_t)bh * F;
+  if (nseg > 0) {
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(s.fold.Wk) +
+                        (s.fold.w_per_head ? (int64_t)(bh % s.fold.H) * kDim * F : 0);
+    stage_wt(smem, W, F, 0, F, tid, NT);
+  }
+  unsigned char* tiles = smem + F * 256 + half * kPartialTileBytes;
+#pragma unroll 1
+  for (int r = 0; 2 * r < nseg; ++r) {
+    const int seg = (2 * r + half < nseg) ? 2 * r + half : -1;
+    {
+      PartialRegs<F> R;
+      segment_sums<F>(R, s.fold, bh, seg, segment_tiles(s.fold, 2 * r), smem, tiles,
+                      tiles + kKTileBytes, htid);
+      if (partial_active<F>(seg, htid)) {
+        float* out = pp + half * E;
+        for_partial<F>(R, htid, [&](int e, float v) { out[e] = v; });
+      }
+    }
+    __syncthreads();   // both partials stored (workgroup scope)
+    const bool pair = 2 * r + 1 < nseg;
+    const bool last = 2 * r + 2 >= nseg;
+#pragma unroll 1
+    for (int e = 4 * tid; e < E; e += 4 * NT) {
+      f32x4 x;
+      if (r > 0)
+        x = *reinterpret_cast<const f32x4*>(xs + e);
+      else if (s.init)
+        x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      else
+        x = *reinterpret_cast<const f32x4*>(e < F * kDim ? S0 + e : z0 + (e - F * kDim));
+      x += *reinterpret_cast<const f32x4*>(pp + e);
+      if (pair) x += *reinterpret_cast<const f32x4*>(pp + E + e);
+      if (last) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(xs + e + i, x[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *reinterpret_cast<f32x4*>(xs + e) = x;
+      }
+    }
+    __syncthreads();   // pp free for the next round
+  }
+  // the new tail: the chunk's last trow rows (16-byte units, four in flight per thread)
+  const int64_t units = s.trow * (kDim * 2 / 16);
+  const u32x4* kc = reinterpret_cast<const u32x4*>(s.kc) +
+                    ((int64_t)bh * s.crow + (s.crow - s.trow)) * (kDim * 2 / 16);
+  const u32x4* vc = reinterpret_cast<const u32x4*>(s.vc) +
+                    ((int64_t)bh * s.crow + (s.crow - s.trow)) * (kDim * 2 / 16);
+  u32x4* kt = reinterpret_cast<u32x4*>(s.ktail) + (int64_t)bh * units;
+  u32x4* vt = reinterpret_cast<u32x4*>(s.vtail) + (int64_t)bh * units;
+#pragma unroll 1
+  for (int64_t u0 = tid; u0 < units; u0 += 4 * NT) {
+    u32x4 kx[4], vx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t u = u0 + (int64_t)j * NT;
+      if (u < units) {
+        kx[j] = kc[u];
+        vx[j] = vc[u];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t u = u0 + (int64_t)j * NT;
+      if (u < units) {
+        kt[u] = kx[j];
+        vt[u] = vx[j];
+      }
+    }
+  }
+  wait_vmem();   // xs's device-scope stores have completed
+}
+
+// The last workgroup of head bh: S, z <- xs (or 0 for a first chunk with nothing folded).
+template <int F>
+__device__ __forceinline__ void finish_head(const StepArgs& s, int bh, int tid) {
+  constexpr int E = F * kDim + F;
+  float* Sd = s.S + (int64_t)bh * F * kDim;
+  float* zd = s.z + (int64_t)bh * F;
+  const float* xs = s.xs + (int64_t)bh * E;
+  const bool copy = s.fold.n_seg > 0;
+  for (int e = 4 * tid; e < E; e += 4 * NT) {
+    float* dst = e < F * kDim ? Sd + e : zd + (e - F * kDim);
+    f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (copy) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[i] = __hip_atomic_load(xs + e + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (copy || s.init) *reinterpret_cast<f32x4*>(dst) = x;
+  }
+}
+
+template <int F>
+__global__ void __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+recurrent_step_bf16_kernel(AttnArgs a, StepArgs s) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  __shared__ float zs[F];
+  __shared__ int bad_flag;
+  __shared__ int last_flag;
+  static_assert(F * 256 + 2 * kPartialTileBytes <= 2 * kStageBytes, "fold tiles exceed LDS");
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int BH = a.nblocks / a.tiles_per_head;
+  int bh;
+  if (b < s.fold_blocks) {
+    if (b >= BH) return;   // padding block: reports nowhere
+    bh = b;
+    fold_head<F>(s, bh, smem, tid);
+  } else {
+    bh = attention_block<F, true, true>(a, b - s.fold_blocks, smem, zs, bad_flag);
+  }
+  __syncthreads();
+  if (tid == 0)
+    last_flag = atomicAdd(s.counter + bh, 1u) == (unsigned)(s.per_head - 1) ? 1 : 0;
+  __syncthreads();
+  if (!last_flag) return;
+  finish_head<F>(s, bh, tid);
+  if (tid == 0)   // ready for the next call
+    __hip_atomic_store(s.counter + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 int attn_bf16_tile_rows() { return QT; }
+
+hipError_t launch_step_bf16(const AttnArgs& a, const StepArgs& s, int F, hipStream_t stream) {
+  dim3 grid(s.fold_blocks + a.nblocks), block(NT);
+  switch (F) {
+    case 64:  hipLaunchKernelGGL(recurrent_step_bf16_kernel<64>, grid, block, 0, stream, a, s); break;
+    case 128: hipLaunchKernelGGL(recurrent_step_bf16_kernel<128>, grid, block, 0, stream, a, s); break;
+    case 256: hipLaunchKernelGGL(recurrent_step_bf16_kernel<256>, grid, block, 0, stream, a, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int F, hipStream_t stream) {
   dim3 grid(a.nblocks), block(NT);

@@ -200,4 +200,22 @@ struct StateArgs {
   const float* zw;
 };
 
+// Single-launch recurrent step (bf16 path): the grid holds fold_blocks workgroups (one per
+// head; the rest of the leading multiple of 8 are idle) ahead of the attention workgroups
+// of the chunk. A head's fold workgroup sums the per-frame partials of the window rows no
+// later window reaches onto S, z in frame order, into xs, and writes the new tail; the last
+// workgroup of the head to finish copies xs into S and z.
+struct StepArgs {
+  StateArgs fold;       // segments (frames) of the rows folded in (part unused)
+  int fold_blocks;      // leading blocks: a multiple of 8, the first BH fold a head
+  int per_head;         // workgroups per head that report to counter[bh]
+  unsigned* counter;    // [BH]: zero before the launch, left zero by it
+  float* xs;            // [BH][F*D + F]: the new S, z of each head
+  float* pp;            // [BH][2][F*D + F]: the two frames' partials of a fold round
+  float* S; float* z;   // carried state [BH][F][D], [BH][F], updated in place
+  int init;             // the state starts empty (first chunk): S = sum of the partials
+  const void* kc; const void* vc; int64_t crow;    // the chunk's K, V: crow rows per head
+  void* ktail; void* vtail; int64_t trow;          // the new tail's K, V: trow = To*HW rows
+};
+
 }  // namespace rehyat

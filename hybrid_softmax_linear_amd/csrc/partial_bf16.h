@@ -1,0 +1,185 @@
+// partial_bf16.h - partial state sums of one row segment on bf16 MFMA (gfx950), D = 128:
+//   dS = phi(K_seg)^T V_seg (F x D, fp32) and dz = sum phi(K_seg), phi(x) = 1 + u + u^2/2,
+//   u = x W / sqrt(D)
+// (the sums s_t, z_t of the chunk-wise RNN, papernotes.org ReHyAt note, key design 4).
+// The body is shared by the state kernel (one segment per 256-thread workgroup) and the
+// single-launch recurrent step (two segments per 512-thread workgroup), so both produce
+// the same bits.
+//
+// U = K W is computed with K rows as the A operand (rows loaded in kappa order) and W^T
+// as the B operand; its C tile has lane = feature and element i = key cidx(i, lane), which
+// is exactly the A operand phi(K)^T of dS = phi(K)^T V. V enters as the B operand from
+// the transposed V^T tile.
+#pragma once
+
+#include "tiles_bf16.h"
+
+namespace rehyat {
+
+// F/32 feature blocks spread over 4 waves.
+template <int F>
+struct FBlocks {
+  static constexpr int total = F / 32;
+  static constexpr int per_wave = total >= 4 ? total / 4 : 1;
+};
+
+// LDS of one segment's tiles (K tile + V^T tile); W^T takes F * 256 more.
+constexpr int kPartialTileBytes = kKTileBytes + kVTileBytes;
+
+// Rows of segment seg: [seg * seg_len, min(+seg_len, n)).
+__device__ __forceinline__ int segment_rows(const StateArgs& a, int seg) {
+  const int64_t r0 = (int64_t)seg * a.seg_len;
+  const int64_t r1 = (r0 + a.seg_len < a.n) ? r0 + a.seg_len : a.n;
+  return (int)(r1 - r0);
+}
+__device__ __forceinline__ int segment_tiles(const StateArgs& a, int seg) {
+  return (segment_rows(a, seg) + kTileRows - 1) / kTileRows;
+}
+
+// Partial sums of segment seg of head bh, left in registers (acc, zp) of 256 threads
+// (tid 0..255) that own the tiles kt, vt. W^T of the head ([F][128], K-tile layout) is in
+// wt, or is being staged there by the workgroup before this call: the loop's first barrier
+// orders it. ntiles: iterations of the tile loop; every thread of the workgroup passes the
+// same value (the loop holds barriers), at least segment_tiles(a, seg). seg < 0: no segment
+// (the threads only take part in the barriers). Element i of acc[p][db] of lane l is
+// dS[32 fb + crow(i, l)][32 db + l mod 32], fb = wave + 4 p; the pair sum of zp[p] is
+// dz[32 fb + l mod 32].
+template <int F>
+struct PartialRegs {
+  f32x16 acc[FBlocks<F>::per_wave][4];
+  float zp[FBlocks<F>::per_wave];
+};
+
+template <int F>
+__device__ __forceinline__ bool partial_active(int seg, int tid) {
+  return (tid >> 6) < FBlocks<F>::total && seg >= 0;
+}
+
+template <int F>
+__device__ __forceinline__ void segment_sums(PartialRegs<F>& R, const StateArgs& a, int bh,
+                                             int seg, int ntiles, const unsigned char* wt,
+                                             unsigned char* kt, unsigned char* vt, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)(seg < 0 ? 0 : seg) * a.seg_len;
+  const int nrows = seg < 0 ? 0 : segment_rows(a, seg);
+
+  // Rows of this segment: global row r0 + w.
+  RowSrc ks, vs;
+  {
+    const uint16_t* ka = reinterpret_cast<const uint16_t*>(a.ka) + head_off(bh, a.a_rows, kDim);
+    const uint16_t* va = reinterpret_cast<const uint16_t*>(a.va) + head_off(bh, a.a_rows, kDim);
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.kb) + head_off(bh, a.b_rows, kDim);
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.vb) + head_off(bh, a.b_rows, kDim);
+    // window-relative row w -> global row r0 + w; A covers global rows [0, na)
+    const int64_t na_rel = (a.na - r0) > 0 ? (a.na - r0) : 0;
+    ks = RowSrc{ka, kb + (r0 > a.na ? (r0 - a.na) * kDim : 0) + a.b_row0 * kDim,
+                a.a_row0 + r0, na_rel, (int64_t)nrows};
+    vs = RowSrc{va, vb + (r0 > a.na ? (r0 - a.na) * kDim : 0) + a.b_row0 * kDim,
+                a.a_row0 + r0, na_rel, (int64_t)nrows};
+  }
+
+  constexpr int PW = FBlocks<F>::per_wave;
+  const bool active = partial_active<F>(seg, tid);
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    R.zp[p] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) R.acc[p][db][i] = 0.0f;
+  }
+
+  TileRegs r;
+  tile_load(r, ks, vs, 0, tid);
+#pragma unroll 1
+  for (int ti = 0; ti < ntiles; ++ti) {
+    __syncthreads();   // previous tile fully consumed (and W^T staged on the first pass)
+    tile_store(r, kt, vt, tid);
+    // the next tile's global loads fly while this tile is reduced
+    if (ti + 1 < ntiles) tile_load(r, ks, vs, (int64_t)(ti + 1) * kTileRows, tid);
+    __syncthreads();
+    if (!active) continue;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key0 = ti * kTileRows + kb * 32;
+      if (key0 >= nrows) break;
+      const int arow = 32 * kb + kappa(lane & 31);
+#pragma unroll
+      for (int p = 0; p < PW; ++p) {
+        const int fb = wave + 4 * p;
+        f32x16 U;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) U[i] = 0.0f;
+        const int brow = 32 * fb + (lane & 31);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int c = 2 * s + (lane >> 5);
+          bf16x8 av = as_bf16x8(lds_read16(kt, ktile_off(arow, c)));
+          bf16x8 bv = as_bf16x8(lds_read16(wt, ktile_off(brow, c)));
+          U = mfma32(av, bv, U);
+        }
+        bf16x8 Pk[2];
+        float zsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i0 = 8 * j + 2 * e;
+            const int key = key0 + cidx(i0, lane);
+            float u0 = U[i0] * a.u_scale, u1 = U[i0 + 1] * a.u_scale;
+            float p0 = (key < nrows) ? 1.0f + u0 + 0.5f * u0 * u0 : 0.0f;
+            float p1 = (key + 1 < nrows) ? 1.0f + u1 + 0.5f * u1 * u1 : 0.0f;
+            unsigned w = pack_bf16_u32(p0, p1);
+            zsum += bf16_lo(w) + bf16_hi(w);
+            pk[e] = w;
+          }
+          Pk[j] = as_bf16x8(pk);
+        }
+        R.zp[p] += zsum;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = 32 * db + (lane & 31);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            bf16x8 bv = as_bf16x8(lds_read16(vt, vtile_chunk_off(d, 4 * kb + 2 * j + (lane >> 5))));
+            R.acc[p][db] = mfma32(Pk[j], bv, R.acc[p][db]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Visit every element of a partial held by this thread: fn(offset in [F*128 + F], value),
+// dS entries at f * 128 + d, dz entries at F * 128 + f (the z sums from lanes < 32).
+template <int F, typename Fn>
+__device__ __forceinline__ void for_partial(const PartialRegs<F>& R, int tid, Fn fn) {
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int p = 0; p < FBlocks<F>::per_wave; ++p) {
+    const int fb = wave + 4 * p;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) fn((32 * fb + crow(i, lane)) * kDim + d, R.acc[p][db][i]);
+    }
+    const float zf = pair_sum(R.zp[p]);
+    if (lane < 32) fn(F * kDim + 32 * fb + lane, zf);
+  }
+}
+
+// Partial sums of segment seg of head bh into a.part[bh][seg] (segment_sums, then stores).
+template <int F>
+__device__ __forceinline__ void segment_partial(const StateArgs& a, int bh, int seg, int ntiles,
+                                                const unsigned char* wt, unsigned char* kt,
+                                                unsigned char* vt, int tid) {
+  PartialRegs<F> R;
+  segment_sums<F>(R, a, bh, seg, ntiles, wt, kt, vt, tid);
+  if (!partial_active<F>(seg, tid)) return;
+  float* out = a.part + ((int64_t)bh * a.n_seg + seg) * (F * kDim + F);
+  for_partial<F>(R, tid, [&](int e, float v) { out[e] = v; });
+}
+
+}  // namespace rehyat

@@ -111,10 +111,10 @@ __device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int ld, int
 // Stage W^T for features [f0, f0+nf) into LDS as [nf][128 d] rows of 256 B, in the K-tile
 // layout (row f, chunk c at c ^ kappa(f & 15)). W is [128 d][F] bf16 (row-major).
 __device__ __forceinline__ void stage_wt(unsigned char* dst, const uint16_t* W, int F, int f0,
-                                         int nf, int tid) {
+                                         int nf, int tid, int nthreads = 256) {
   // pairs (d, chunk of 8 features): thread reads W[d][f0 + 8c .. +8]
   const int pairs = kDim * (nf / 8);
-  for (int id = tid; id < pairs; id += 256) {
+  for (int id = tid; id < pairs; id += nthreads) {
     int d = id & (kDim - 1), c = id >> 7;
     u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)d * F + f0 + c * 8);
 #pragma unroll

@@ -13,7 +13,8 @@ import torch
 from . import (BF16, BIDIR, CAUSAL, F32, PHI_ELU, PHI_MLP, PHI_POLY2, Desc, rehyat_hybrid_bwd,
                rehyat_hybrid_bwd_workspace, rehyat_hybrid_fwd, rehyat_hybrid_fwd_stats,
                rehyat_hybrid_fwd_workspace, rehyat_phi, rehyat_recurrent_step,
-               rehyat_recurrent_step_workspace, rehyat_state_update,
+               rehyat_recurrent_step_workspace, rehyat_recurrent_step_fused,
+               rehyat_recurrent_step_fused_workspace, rehyat_state_update,
                rehyat_state_update_workspace)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -141,31 +142,61 @@ def state_update(k, v, Wk, S, z, fmap: Optional[FeatureMap] = None) -> None:
 
 class Recurrent:
     """Chunk-wise RNN form: carries S [B,H,F,D], z [B,H,F] (fp32) and the K/V tail of the
-    last To frames; memory is allocated once, at construction."""
+    last To frames; memory is allocated once, at construction.
+
+    fused: run each step as one launch (rehyat_recurrent_step_fused, which writes the new
+    tail to a second buffer: the two alternate); None picks it where it is supported (bf16
+    inputs, the fixed feature map)."""
 
     def __init__(self, B: int, H: int, D: int, F: int, *, T: int, HW: int, Tc: int, To: int,
                  dtype: torch.dtype = torch.bfloat16, y_dtype: torch.dtype = torch.float32,
-                 w_per_head: bool = False, device="cuda", fmap: Optional[FeatureMap] = None):
+                 w_per_head: bool = False, device="cuda", fmap: Optional[FeatureMap] = None,
+                 fused: Optional[bool] = None):
         fm = fmap or FeatureMap()
         self.desc = Desc(B=B, H=H, T=T, HW=HW, D=D, F=F, Tc=Tc, To=To, dtype=_DT[dtype],
                          y_dtype=_DT[y_dtype], mode=CAUSAL, w_per_head=int(w_per_head),
                          phi_kind=fm.kind, phi_hidden=fm.hidden, phi_parts=fm.parts)
         self.S = torch.zeros((B, H, F, D), dtype=torch.float32, device=device)
         self.z = torch.zeros((B, H, F), dtype=torch.float32, device=device)
+        if fused is None:
+            fused = dtype == torch.bfloat16 and fm.kind == PHI_POLY2
+        self.fused = bool(fused)
         rows = max(To * HW, 1)
-        self.k_tail = torch.zeros((B, H, rows, D), dtype=dtype, device=device)
-        self.v_tail = torch.zeros((B, H, rows, D), dtype=dtype, device=device)
-        self.ws = workspace(rehyat_recurrent_step_workspace(self.desc), device)
+        self._tails = [(torch.zeros((B, H, rows, D), dtype=dtype, device=device),
+                        torch.zeros((B, H, rows, D), dtype=dtype, device=device))
+                       for _ in range(2 if self.fused else 1)]
+        self._cur = 0
+        if self.fused:
+            # completion counters at its start: zero before the first call, left zero
+            self.ws = torch.zeros(max(rehyat_recurrent_step_fused_workspace(self.desc), 16),
+                                  dtype=torch.uint8, device=device)
+        else:
+            self.ws = workspace(rehyat_recurrent_step_workspace(self.desc), device)
         self.y_dtype = y_dtype
         self.t = 0
+
+    @property
+    def k_tail(self) -> torch.Tensor:
+        return self._tails[self._cur][0]
+
+    @property
+    def v_tail(self) -> torch.Tensor:
+        return self._tails[self._cur][1]
 
     def step(self, q_c, k_c, v_c, Wq, Wk=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         Wk = Wq if Wk is None else Wk
         y = torch.empty(q_c.shape, dtype=self.y_dtype, device=q_c.device) if out is None else out
-        tail_k = self.k_tail if self.desc.To > 0 else None
-        tail_v = self.v_tail if self.desc.To > 0 else None
-        rehyat_recurrent_step(self.desc, self.t, q_c, k_c, v_c, Wq, Wk, self.S, self.z, tail_k,
-                              tail_v, y, self.ws)
+        has_tail = self.desc.To > 0
+        kt, vt = (self.k_tail, self.v_tail) if has_tail else (None, None)
+        if self.fused:
+            nxt = 1 - self._cur
+            ko, vo = self._tails[nxt] if has_tail else (None, None)
+            rehyat_recurrent_step_fused(self.desc, self.t, q_c, k_c, v_c, Wq, Wk, self.S, self.z,
+                                        kt, vt, ko, vo, y, self.ws)
+            self._cur = nxt
+        else:
+            rehyat_recurrent_step(self.desc, self.t, q_c, k_c, v_c, Wq, Wk, self.S, self.z, kt,
+                                  vt, y, self.ws)
         self.t += 1
         return y
 

@@ -170,6 +170,33 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* desc, int32_t chunk_index
                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * rehyat_recurrent_step as one kernel launch (key design 4's chunk-wise RNN, for streaming
+ * where a step is short and launch gaps would show): the chunk's attention, the per-frame
+ * sums of the window rows no later window reaches, their fold into S and z and the new
+ * tail come from a single launch. Arguments, requirements and results as for
+ * rehyat_recurrent_step, bit for bit, except that the tail has separate input and output
+ * buffers (a caller alternates two):
+ *   k_tail, v_tail [B, H, To*HW, D] dtype (device, read): the K and V rows of the To frames
+ *           before the chunk (ignored for t = 0). May be NULL when To = 0.
+ *   k_tail_out, v_tail_out [B, H, To*HW, D] dtype (device, written): those of the chunk's
+ *           last To frames; they must not overlap any other buffer of the call. May be NULL
+ *           when To = 0.
+ *   ws   device scratch of at least rehyat_recurrent_step_fused_workspace(desc) bytes.
+ *        Its first B*H*4 bytes are per-head completion counters: they must be zero before
+ *        the first call (zero the whole workspace once when allocating it); every call
+ *        leaves them zero. Two calls must not use one workspace at the same time.
+ * Supported: dtype bf16 (D = 128, F in {64, 128, 256}) with phi_kind REHYAT_PHI_POLY2;
+ * other descriptors return REHYAT_ERR_UNSUPPORTED (use rehyat_recurrent_step).
+ */
+size_t rehyat_recurrent_step_fused_workspace(const rehyat_desc* desc);
+rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* desc, int32_t chunk_index,
+                                          const void* q_c, const void* k_c, const void* v_c,
+                                          const void* Wq, const void* Wk, float* S, float* z,
+                                          const void* k_tail, const void* v_tail,
+                                          void* k_tail_out, void* v_tail_out, void* y_c,
+                                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Backward of the non-recursive causal form (key designs 1 and 4: the form the method is
  * trained and its feature maps distilled with): the gradients of sum(dy * y) for
  * y = rehyat_hybrid_fwd(q, k, v, Wq, Wk), the fixed feature map.
@@ -204,7 +231,8 @@ const char* rehyat_last_error(void);
  * Kernel timing (measurement aid). While enabled, every launch of one kernel is bracketed
  * by HIP events recorded on the launch stream (events are created once, at most 4096
  * launches are recorded). The argument selects it: 1 the hybrid-attention kernel of the
- * forward, 2 the dk/dv kernel and 3 the dq kernel of rehyat_hybrid_bwd; 0 disables.
+ * forward and of rehyat_recurrent_step, 2 the dk/dv kernel and 3 the dq kernel of
+ * rehyat_hybrid_bwd, 4 the kernel of rehyat_recurrent_step_fused; 0 disables.
  * rehyat_timing_read synchronises on the last recorded event and returns the summed kernel
  * time in milliseconds and the launch count, then clears the record. Enabling clears the
  * record too. Not thread-safe.

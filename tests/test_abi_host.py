@@ -129,6 +129,44 @@ def test_recurrent_step_validation():
     assert step(d, S=P[5], z=P[5] + 16) == ERR_ALIAS       # z inside S
 
 
+def step_fused(desc, t=1, q=P[0], k=P[1], v=P[2], Wq=P[3], Wk=P[4], S=P[5], z=P[6], kt=P[7],
+               vt=P[8], y=P[9], ws=P[10], ko=P[11], vo=P[12], ws_bytes=None):
+    L = hs.lib()
+    if ws_bytes is None:
+        ws_bytes = L.rehyat_recurrent_step_fused_workspace(ctypes.byref(desc.c()))
+    return L.rehyat_recurrent_step_fused(ctypes.byref(desc.c()), t, q, k, v, Wq, Wk, S, z, kt, vt,
+                                         ko, vo, y, ws, ws_bytes, None)
+
+
+def test_recurrent_step_fused_validation():
+    """The single-launch step takes the step's checks, and supports bf16 with the fixed map
+    only; every case below returns before any launch."""
+    d = _desc()
+    assert step_fused(_desc(To=4)) == ERR_UNSUP
+    assert step_fused(d, t=-1) == ERR_SHAPE
+    assert step_fused(d, t=d.n_chunks) == ERR_SHAPE
+    assert step_fused(_desc(T=7, Tc=3, To=2), t=2) == ERR_UNSUP
+    assert step_fused(d, kt=None) == ERR_NULL
+    assert step_fused(d, z=P[5] + 4) == ERR_ALIGN
+    assert step_fused(d, ws=P[10] + 8) == ERR_ALIGN
+    assert step_fused(d, ws_bytes=0) == ERR_WS
+    assert step_fused(d, y=P[2]) == ERR_ALIAS
+    assert step_fused(_desc(dtype=hs.F32, D=64)) == ERR_UNSUP
+    assert step_fused(_desc(phi_kind=hs.PHI_ELU)) == ERR_UNSUP
+    assert step_fused(_desc(phi_kind=hs.PHI_MLP, phi_hidden=128, phi_parts=2)) == ERR_UNSUP
+    assert step_fused(d, ko=None) == ERR_NULL                  # new tail needed when To > 0
+    assert step_fused(d, vo=P[12] + 8) == ERR_ALIGN
+    assert step_fused(d, ko=P[7]) == ERR_ALIAS                 # new tail over the carried one
+    assert step_fused(d, vo=P[1]) == ERR_ALIAS                 # new tail over k_c
+    assert step_fused(d, ko=P[11], vo=P[11] + 16) == ERR_ALIAS
+    L = hs.lib()
+    BH, E = d.B * d.H, d.F * d.D + d.F
+    # per-head counters (rounded up to 256 bytes), then the new state and two frames' partials
+    assert L.rehyat_recurrent_step_fused_workspace(ctypes.byref(d.c())) == (
+        max(256, -(-BH * 4 // 256) * 256) + 3 * BH * E * 4)
+    assert L.rehyat_recurrent_step_fused_workspace(ctypes.byref(_desc(D=64).c())) == 0
+
+
 def test_phi_and_state_update_validation():
     L = hs.lib()
     d = _desc()

@@ -53,15 +53,16 @@ def test_full_workload_whole_sequence(i):
     _check_rows(y_rows, ref, inp, cfg, rows, cfg.name)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["multi_launch", "single_launch"])
 @pytest.mark.parametrize("i", [3, 5])
-def test_full_workload_recurrent_equals_whole(i):
-    """The causal workloads run as the chunk-wise RNN (one call per chunk) give exactly the
-    whole-sequence result."""
+def test_full_workload_recurrent_equals_whole(i, fused):
+    """The causal workloads run as the chunk-wise RNN (one call per chunk, multi-launch or
+    single-launch steps) give exactly the whole-sequence result."""
     cfg = syn.config(i)
     inp = syn.make_inputs(cfg)
     d, y = _fwd(cfg, inp)
     rec = ta.Recurrent(cfg.B, cfg.H, cfg.D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
-                       device=DEV)
+                       device=DEV, fused=fused)
     Np = cfg.Tc * cfg.HW
     for t in range(cfg.n_chunks):
         r0, r1 = t * Np, min((t + 1) * Np, cfg.N)
@@ -70,17 +71,20 @@ def test_full_workload_recurrent_equals_whole(i):
         assert torch.equal(yc, y[:, :, r0:r1]), f"chunk {t} differs"
 
 
-def test_streaming_81_frames_flat_memory():
-    """27 recurrent steps over the 81-frame latent: host chunks are copied into fixed device
-    buffers, device memory stays flat, outputs match the oracle on sampled rows and the
-    whole-sequence form bitwise."""
+@pytest.mark.parametrize("fused", [False, True], ids=["multi_launch", "single_launch"])
+def test_streaming_81_frames_flat_memory(fused):
+    """27 recurrent steps over the 81-frame latent (rehyat_recurrent_step, or
+    rehyat_recurrent_step_fused): host chunks are copied into fixed device buffers, device
+    memory stays flat, outputs match the oracle on sampled rows and the whole-sequence form
+    bitwise."""
     cfg = syn.config(4)
     inp = syn.make_inputs(cfg)
     B, H, D, Np = cfg.B, cfg.H, cfg.D, cfg.Tc * cfg.HW
     W = inp["W"].to(DEV)
     bufs = [torch.empty((B, H, Np, D), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
     y_c = torch.empty((B, H, Np, D), dtype=torch.float32, device=DEV)
-    rec = ta.Recurrent(B, H, D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, device=DEV)
+    rec = ta.Recurrent(B, H, D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, device=DEV,
+                       fused=fused)
     rows = pu.sample_rows(cfg.T, cfg.HW, cfg.Tc, per_edge=6, n_random=16, seed=4)
     rows_by_chunk = {}
     for r in rows:
@@ -107,7 +111,8 @@ def test_streaming_81_frames_flat_memory():
     assert len(set(m[1] for m in mem)) == 1, f"peak device memory grew: {mem}"
     y_rows = np.stack([got[r] for r in rows], axis=2)
     ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=True, rows=rows)
-    _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + " streamed")
+    _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + (" streamed, one launch per step"
+                                                          if fused else " streamed"))
     del bufs, y_c, rec
     d, y = _fwd(cfg, inp)
     assert torch.equal(streamed, y)

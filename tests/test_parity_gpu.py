@@ -175,16 +175,21 @@ def test_state_update(dtype, D, F, n):
 
 # ---- the chunk-wise RNN form --------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,T,HW,F,Tc,To", [("bf16", 9, 80, 128, 3, 1), ("bf16", 8, 80, 128, 3, 2),
-                                                ("bf16", 10, 60, 256, 7, 3), ("bf16", 6, 50, 64, 2, 0),
-                                                ("f32", 8, 40, 64, 2, 1)])
-def test_recurrent_steps_equal_whole_sequence(dtype, T, HW, F, Tc, To):
+@pytest.mark.parametrize("dtype,T,HW,F,Tc,To,fused", [
+    ("bf16", 9, 80, 128, 3, 1, False), ("bf16", 9, 80, 128, 3, 1, True),
+    ("bf16", 8, 80, 128, 3, 2, False), ("bf16", 8, 80, 128, 3, 2, True),
+    ("bf16", 10, 60, 256, 7, 3, False), ("bf16", 10, 60, 256, 7, 3, True),
+    ("bf16", 6, 50, 64, 2, 0, False), ("bf16", 6, 50, 64, 2, 0, True),
+    ("f32", 8, 40, 64, 2, 1, False)])
+def test_recurrent_steps_equal_whole_sequence(dtype, T, HW, F, Tc, To, fused):
+    """rehyat_recurrent_step (fused=False) and rehyat_recurrent_step_fused, chunk by chunk."""
     B, H = 1, 2
     D = 128 if dtype == "bf16" else 64
     inp = syn.make_custom(B, H, T * HW, D, F, seed=9, dtype=dtype, HW=HW)
     d = {k: v.to(DEV) for k, v in inp.items()}
     whole = ta.hybrid_fwd(d["q"], d["k"], d["v"], d["W"], HW=HW, Tc=Tc, To=To, causal=True)
-    rec = ta.Recurrent(B, H, D, F, T=T, HW=HW, Tc=Tc, To=To, dtype=syn.TORCH_DTYPE[dtype])
+    rec = ta.Recurrent(B, H, D, F, T=T, HW=HW, Tc=Tc, To=To, dtype=syn.TORCH_DTYPE[dtype],
+                       fused=fused)
     outs = []
     Np = Tc * HW
     for t in range(-(-T // Tc)):
@@ -206,7 +211,7 @@ def test_recurrent_steps_equal_whole_sequence(dtype, T, HW, F, Tc, To):
         assert (np.abs(S[0, h] - Sr) <= tol).all()
     ref = pu.oracle_rows(inp, HW=HW, Tc=Tc, To=To, causal=True)
     _check(streamed.double().cpu().numpy(), ref, inp, bf16=dtype == "bf16", y_bf16=False, T=T,
-           HW=HW, Tc=Tc, label=f"stream {dtype} T{T} Tc{Tc} To{To}")
+           HW=HW, Tc=Tc, label=f"stream {dtype} T{T} Tc{Tc} To{To} fused={fused}")
 
 
 def test_recurrent_snapshot_resume():
