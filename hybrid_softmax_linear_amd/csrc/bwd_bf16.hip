@@ -432,13 +432,18 @@ bwd_dq_kernel(BwdArgs a) {
 // Window part: for every chunk whose window holds the keys (the keys' own chunk and the
 // next ones whose overlap reaches back to them), per 32-query block: S = Q K^T and
 // dP = dY V^T (rows of Q and dY in kappa order, so the results are B operands over
-// queries), p and ds, dv^T += dY^T p, dk^T += Q^T ds (transposing LDS reads). Linear part,
+// queries), p and ds, dv^T += dY^T p, dk^T += Q^T ds (transposing LDS reads). The kernel
+// runs one wave per SIMD (K, V fragments and both accumulators live in registers), so
+// nothing hides a wave's own latencies: 128-query tiles are double-buffered, each block's
+// LDS fragments are read as one batch, and the S, dP MFMAs of two blocks run ahead of
+// their exponentials. Linear part,
 // per key frame present in the tile: U^T = W^T K^T, (G v)^T, phi(k), dphi(k) = G v - h,
 // gk = dphi (1 + u) / sqrt(D), dv^T += G^T phi(k)^T, dk^T += W gk^T, for the lanes whose key
 // lies in that frame.
 constexpr int kKW = 4;                                    // waves of the dk/dv kernel
-constexpr int kQTile = 64;
-constexpr int kDkLds = kLinLds > 2 * kQTile * kRowB ? kLinLds : 2 * kQTile * kRowB;
+constexpr int kQTile = 128;
+constexpr int kQBuf = 2 * kQTile * kRowB + 2 * kQTile * 4;   // Q, dY rows; lse, dy.y
+constexpr int kDkLds = kLinLds > 2 * kQBuf ? kLinLds : 2 * kQBuf;
 
 template <int F>
 __global__ void __launch_bounds__(64 * kKW)
@@ -446,7 +451,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   constexpr int FS = F < 128 ? F : 128;
   constexpr int RW = 2 * FS + 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kDkLds];
-  __shared__ float sL[kQTile], sD[kQTile], hs[F];
+  __shared__ float hs[F];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int kt;
   const BwdGeo g = bwd_geo(a, blockIdx.x, kt);
@@ -473,50 +478,112 @@ bwd_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) dK[db][i] = dV[db][i] = 0.0f;
   const float ls = a.logit_scale, us = a.u_scale;
   const int ab = kappa(lane & 31) * kRowB + 16 * (lane >> 5);
-  unsigned char* sQ = smem;
-  unsigned char* sY = smem + kQTile * kRowB;
   const int64_t Np = (int64_t)a.Tc * a.HW;
   const int64_t tile_end = g.row0 + (kt * 128 + 128 < g.rows ? kt * 128 + 128 : g.rows);
 
   // ---- window part: the key's own chunk and later chunks whose window reaches back ----
+  // Query tiles (chunk tq, rows q0 .. q0 + kQTile) are double-buffered: tile n + 1's Q, dY,
+  // lse and dy.y rows stream into the other buffer by direct-to-LDS loads while tile n is
+  // reduced. Rows past the chunk come back as zeros (Q = dY = 0 makes every term zero).
+  auto chunk_lo = [&](int tq) {
+    const int64_t r = tq * Np - (int64_t)a.To * a.HW;
+    return r > 0 ? r : (int64_t)0;
+  };
+  auto chunk_rows = [&](int tq) {
+    const int64_t r0 = tq * Np;
+    return (int)((r0 + Np < a.N) ? Np : a.N - r0);
+  };
+  auto issue = [&](int tq, int q0, int b) {
+    const int64_t r0 = tq * Np + q0;
+    const int bytes = (chunk_rows(tq) - q0) * 256;
+    unsigned char* base = smem + b * kQBuf;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const uint16_t*>(a.q) + (hrow + r0) * kDim), (short)0, bytes,
+        kBufWord3);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.dyb + (hrow + r0) * kDim), (short)0, bytes, kBufWord3);
+    dma_rows<kQTile, kKW>(qr, base, wave, lane);
+    dma_rows<kQTile, kKW>(yr, base + kQTile * kRowB, wave, lane);
+    // lse and dy.y of the tile: 4 bytes per lane, one instruction per 64 rows each
+    const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.lse + hrow + r0), (short)0, bytes / 64, kBufWord3);
+    const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.dvec + hrow + r0), (short)0, bytes / 64, kBufWord3);
+    if (wave < kQTile / 64) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          lr, (lds_void*)(base + 2 * kQTile * kRowB + wave * 256), 4, (wave * 64 + lane) * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          dr, (lds_void*)(base + 2 * kQTile * kRowB + kQTile * 4 + wave * 256), 4,
+          (wave * 64 + lane) * 4, 0, 0, 0);
+    }
+  };
+  int tq = g.t, q0 = 0, qbuf = 0;
+  bool have = tq < a.n_chunks && chunk_lo(tq) < tile_end;
+  if (have) issue(tq, q0, 0);
 #pragma unroll 1
-  for (int tq = g.t; tq < a.n_chunks; ++tq) {
-    const int64_t qrow0 = tq * Np;
-    const int64_t qend = (qrow0 + Np < a.N) ? qrow0 + Np : a.N;
-    const int64_t lo_q = qrow0 - (int64_t)a.To * a.HW > 0 ? qrow0 - (int64_t)a.To * a.HW : 0;
-    if (lo_q >= tile_end) break;                          // no key of the tile in this window
-    const int nq = (int)(qend - qrow0);
-    const bool key_in = ok && key >= lo_q;
-#pragma unroll 1
-    for (int q0 = 0; q0 < nq; q0 += kQTile) {
-      __syncthreads();
-      const int bytes = (nq - q0) * 256;
-      const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(reinterpret_cast<const uint16_t*>(a.q) + (hrow + qrow0 + q0) * kDim), (short)0, bytes,
-          kBufWord3);
-      const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.dyb + (hrow + qrow0 + q0) * kDim), (short)0, bytes, kBufWord3);
-      dma_rows<kQTile, kKW>(qr, sQ, wave, lane);
-      dma_rows<kQTile, kKW>(yr, sY, wave, lane);
-      if (tid < kQTile) {
-        const bool in = q0 + tid < nq;
-        sL[tid] = in ? a.lse[hrow + qrow0 + q0 + tid] : 1.0e30f;
-        sD[tid] = in ? a.dvec[hrow + qrow0 + q0 + tid] : 0.0f;
-      }
-      wait_vmem_all();
-      __syncthreads();
-      if (!active) continue;
-#pragma unroll 1
-      for (int qb = 0; qb < kQTile / 32; ++qb) {
-        if (q0 + 32 * qb >= nq) break;
-        f32x16 S, P;
+  while (have) {
+    int ntq = tq, nq0 = q0 + kQTile;
+    if (nq0 >= chunk_rows(tq)) {
+      ntq = tq + 1;
+      nq0 = 0;
+    }
+    const bool nhave = ntq < a.n_chunks && chunk_lo(ntq) < tile_end;
+    wait_vmem_all();
+    __syncthreads();   // tile landed everywhere; the other buffer's last reader is done
+    if (nhave) issue(ntq, nq0, qbuf ^ 1);
+    const unsigned char* sQ = smem + qbuf * kQBuf;
+    const unsigned char* sY = sQ + kQTile * kRowB;
+    const float* sL = reinterpret_cast<const float*>(sQ + 2 * kQTile * kRowB);
+    const float* sD = sL + kQTile;
+    const bool key_in = ok && key >= chunk_lo(tq);
+    tq = ntq;
+    q0 = nq0;
+    have = nhave;
+    qbuf ^= 1;
+    if (!active) continue;
+    // The tile's 32-query blocks in pairs: the S and dP MFMAs of both blocks of a pair
+    // first, then each block's p and ds (while the other block's MFMAs run) and its dv, dk
+    // MFMAs. Every block's LDS operand fragments are read as one batch before its MFMAs.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[i] = P[i] = 0.0f;
+    for (int pr = 0; pr < kQTile / 32; pr += 2) {
+      f32x16 S[2], Pd[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qb = pr + h2;
+        bf16x8 qf[8], yf[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          S = mfma32(as_bf16x8(lds_read16(sQ, ab + qb * 32 * kRowB + 32 * s)), Kf[s], S);
-          P = mfma32(as_bf16x8(lds_read16(sY, ab + qb * 32 * kRowB + 32 * s)), Vf[s], P);
+          qf[s] = as_bf16x8(lds_read16(sQ, ab + qb * 32 * kRowB + 32 * s));
+          yf[s] = as_bf16x8(lds_read16(sY, ab + qb * 32 * kRowB + 32 * s));
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[h2][i] = Pd[h2][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          S[h2] = mfma32(qf[s], Kf[s], S[h2]);
+          Pd[h2] = mfma32(yf[s], Vf[s], Pd[h2]);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qb = pr + h2;
+        // this lane's query statistics: element i holds query 32 qb + cidx(i, lane), two
+        // runs of 8 consecutive queries
+        f32x4 Lq[4], Dq[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = 32 * qb + 16 * (r >> 1) + 8 * (lane >> 5) + 4 * (r & 1);
+          Lq[r] = *reinterpret_cast<const f32x4*>(sL + qi);
+          Dq[r] = *reinterpret_cast<const f32x4*>(sD + qi);
+        }
+        bf16x8 yt[4][2], qt[4][2];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            yt[db][j] = frag_tr(sY, kRowB, 32 * qb + 16 * j, 32 * db, lane);
+            qt[db][j] = frag_tr(sQ, kRowB, 32 * qb + 16 * j, 32 * db, lane);
+          }
         bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -527,10 +594,11 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
               const int i = 8 * j + 2 * e + q2;
-              const int ql = 32 * qb + cidx(i, lane);      // query within the tile
-              const float p = key_in ? fast_exp2(S[i] * ls - sL[ql]) : 0.0f;
+              const float Lv = Lq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
+              const float Dv = Dq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
+              const float p = key_in ? fast_exp2(S[h2][i] * ls - Lv) : 0.0f;
               p2[q2] = p;
-              d2[q2] = p * (P[i] - sD[ql]) * us;
+              d2[q2] = p * (Pd[h2][i] - Dv) * us;
             }
             pp[e] = pack_bf16_u32(p2[0], p2[1]);
             pd[e] = pack_bf16_u32(d2[0], d2[1]);
@@ -542,8 +610,8 @@ bwd_dkdv_kernel(BwdArgs a) {
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            dV[db] = mfma32(frag_tr(sY, kRowB, 32 * qb + 16 * j, 32 * db, lane), pb[j], dV[db]);
-            dK[db] = mfma32(frag_tr(sQ, kRowB, 32 * qb + 16 * j, 32 * db, lane), dsb[j], dK[db]);
+            dV[db] = mfma32(yt[db][j], pb[j], dV[db]);
+            dK[db] = mfma32(qt[db][j], dsb[j], dK[db]);
           }
       }
     }
