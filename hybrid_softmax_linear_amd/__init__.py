@@ -121,6 +121,10 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(library_path):
             raise RuntimeError(f"{library_path} is missing: build it with "
                                "`python -m hybrid_softmax_linear_amd.build`")
+        # torch first: librehyat.so then binds to the HIP runtime torch has loaded, the one
+        # that owns the streams and device memory handed to it (loaded the other way round,
+        # the process would hold two runtimes)
+        import torch  # noqa: F401
         L = ctypes.CDLL(library_path)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)

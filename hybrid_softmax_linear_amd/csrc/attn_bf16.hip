@@ -775,11 +775,15 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 // than the whole fold.)
 
 // The fold workgroup of head bh: xs = ((S + p_0) + p_1) + ... over the nseg frames (S taken
-// as 0 for the first chunk), then the new tail. Each round the two halves form two frames'
-// partials and store them (pp: [2][F*D + F]); then all threads add them on elementwise.
+// as 0 for the first chunk), then the new tail. Each round the two halves of the workgroup
+// form two frames' partials (F <= 128) or the two halves of one frame's (F = 256, whose
+// four feature blocks per wave would not fit beside the attention code's registers) and
+// store them (pp: [2][F*D + F]); then all threads add them on elementwise, in frame order.
 template <int F>
 __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned char* smem, int tid) {
   constexpr int E = F * kDim + F;
+  constexpr bool kSplit = F > 128;
+  constexpr int kPer = kSplit ? 1 : 2;   // frames per round
   const int nseg = s.fold.n_seg;
   const int half = tid >> 8, htid = tid & 255;
   float* xs = s.xs + (int64_t)bh * E;
@@ -793,9 +797,23 @@ __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned ch
   }
   unsigned char* tiles = smem + F * 256 + half * kPartialTileBytes;
 #pragma unroll 1
-  for (int r = 0; 2 * r < nseg; ++r) {
-    const int seg = (2 * r + half < nseg) ? 2 * r + half : -1;
-    {
+  for (int r = 0; kPer * r < nseg; ++r) {
+    if (kSplit) {
+      const int seg = r;
+      const int ntiles = segment_tiles(s.fold, seg);
+      if (half == 0) {
+        PartialRegs<F, 0> R;
+        segment_sums<F, 0>(R, s.fold, bh, seg, ntiles, smem, tiles, tiles + kKTileBytes, htid);
+        if (partial_active<F, 0>(seg, htid))
+          for_partial<F, 0>(R, htid, [&](int e, float v) { pp[e] = v; });
+      } else {
+        PartialRegs<F, 1> R;
+        segment_sums<F, 1>(R, s.fold, bh, seg, ntiles, smem, tiles, tiles + kKTileBytes, htid);
+        if (partial_active<F, 1>(seg, htid))
+          for_partial<F, 1>(R, htid, [&](int e, float v) { pp[e] = v; });
+      }
+    } else {
+      const int seg = (2 * r + half < nseg) ? 2 * r + half : -1;
       PartialRegs<F> R;
       segment_sums<F>(R, s.fold, bh, seg, segment_tiles(s.fold, 2 * r), smem, tiles,
                       tiles + kKTileBytes, htid);
@@ -804,9 +822,9 @@ __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned ch
         for_partial<F>(R, htid, [&](int e, float v) { out[e] = v; });
       }
     }
-    __syncthreads();   // both partials stored (workgroup scope)
-    const bool pair = 2 * r + 1 < nseg;
-    const bool last = 2 * r + 2 >= nseg;
+    __syncthreads();   // the round's partials stored (workgroup scope)
+    const bool pair = !kSplit && 2 * r + 1 < nseg;
+    const bool last = kPer * r + kPer >= nseg;
 #pragma unroll 1
     for (int e = 4 * tid; e < E; e += 4 * NT) {
       f32x4 x;

@@ -44,21 +44,31 @@ __device__ __forceinline__ int segment_tiles(const StateArgs& a, int seg) {
 // (the threads only take part in the barriers). Element i of acc[p][db] of lane l is
 // dS[32 fb + crow(i, l)][32 db + l mod 32], fb = wave + 4 p; the pair sum of zp[p] is
 // dz[32 fb + l mod 32].
-template <int F>
-struct PartialRegs {
-  f32x16 acc[FBlocks<F>::per_wave][4];
-  float zp[FBlocks<F>::per_wave];
+// Split form (kPart >= 0, F = 256): the 256 threads take the feature blocks 4 kPart ..
+// 4 kPart + 3 only (one per wave), so that two groups of 256 threads form one segment's
+// partial together with half the accumulators each.
+template <int F, int kPart = -1>
+struct PartialShape {
+  static constexpr int PW = kPart >= 0 ? 1 : FBlocks<F>::per_wave;   // blocks per wave
+  __device__ static int fb(int wave, int p) { return kPart >= 0 ? 4 * kPart + wave : wave + 4 * p; }
 };
 
-template <int F>
+template <int F, int kPart = -1>
+struct PartialRegs {
+  f32x16 acc[PartialShape<F, kPart>::PW][4];
+  float zp[PartialShape<F, kPart>::PW];
+};
+
+template <int F, int kPart = -1>
 __device__ __forceinline__ bool partial_active(int seg, int tid) {
-  return (tid >> 6) < FBlocks<F>::total && seg >= 0;
+  return PartialShape<F, kPart>::fb(tid >> 6, 0) < FBlocks<F>::total && seg >= 0;
 }
 
-template <int F>
-__device__ __forceinline__ void segment_sums(PartialRegs<F>& R, const StateArgs& a, int bh,
-                                             int seg, int ntiles, const unsigned char* wt,
-                                             unsigned char* kt, unsigned char* vt, int tid) {
+template <int F, int kPart = -1>
+__device__ __forceinline__ void segment_sums(PartialRegs<F, kPart>& R, const StateArgs& a,
+                                             int bh, int seg, int ntiles,
+                                             const unsigned char* wt, unsigned char* kt,
+                                             unsigned char* vt, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t r0 = (int64_t)(seg < 0 ? 0 : seg) * a.seg_len;
   const int nrows = seg < 0 ? 0 : segment_rows(a, seg);
@@ -78,8 +88,8 @@ __device__ __forceinline__ void segment_sums(PartialRegs<F>& R, const StateArgs&
                 a.a_row0 + r0, na_rel, (int64_t)nrows};
   }
 
-  constexpr int PW = FBlocks<F>::per_wave;
-  const bool active = partial_active<F>(seg, tid);
+  constexpr int PW = PartialShape<F, kPart>::PW;
+  const bool active = partial_active<F, kPart>(seg, tid);
 #pragma unroll
   for (int p = 0; p < PW; ++p) {
     R.zp[p] = 0.0f;
@@ -106,7 +116,7 @@ __device__ __forceinline__ void segment_sums(PartialRegs<F>& R, const StateArgs&
       const int arow = 32 * kb + kappa(lane & 31);
 #pragma unroll
       for (int p = 0; p < PW; ++p) {
-        const int fb = wave + 4 * p;
+        const int fb = PartialShape<F, kPart>::fb(wave, p);
         f32x16 U;
 #pragma unroll
         for (int i = 0; i < 16; ++i) U[i] = 0.0f;
@@ -153,12 +163,12 @@ __device__ __forceinline__ void segment_sums(PartialRegs<F>& R, const StateArgs&
 
 // Visit every element of a partial held by this thread: fn(offset in [F*128 + F], value),
 // dS entries at f * 128 + d, dz entries at F * 128 + f (the z sums from lanes < 32).
-template <int F, typename Fn>
-__device__ __forceinline__ void for_partial(const PartialRegs<F>& R, int tid, Fn fn) {
+template <int F, int kPart = -1, typename Fn>
+__device__ __forceinline__ void for_partial(const PartialRegs<F, kPart>& R, int tid, Fn fn) {
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int p = 0; p < FBlocks<F>::per_wave; ++p) {
-    const int fb = wave + 4 * p;
+  for (int p = 0; p < PartialShape<F, kPart>::PW; ++p) {
+    const int fb = PartialShape<F, kPart>::fb(wave, p);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int d = 32 * db + (lane & 31);
