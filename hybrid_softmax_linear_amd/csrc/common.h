@@ -124,9 +124,11 @@ struct AttnArgs {
   // head strides. For the whole-sequence form A is the sequence itself and nb = 0.
   const void* ka; const void* va; int64_t a_rows;
   const void* kb; const void* vb; int64_t b_rows;
-  // The bf16 kernel reads K and V of the window from segment A alone: the whole sequence
-  // (window of chunk t at rows [lo, hi)) or, with step set, a gathered window (rows
-  // [0, hi - lo)), a_rows rows per head.
+  // The bf16 attention kernel reads K and V of the window from segment A alone: the whole
+  // sequence (window of chunk t at rows [lo, hi)) or, with step set, a gathered window
+  // (rows [0, hi - lo)), a_rows rows per head. The single-launch step kernel reads the
+  // window's first na = c0 - lo rows from the last na rows of A (the carried tail) and the
+  // rest from B (the chunk), as the fp32 kernel does.
   const void* Wq;       // [D, F] or [H, D, F]
   int w_per_head;
   const float* S;       // linear state of (head, chunk): S + bh*s_bh + t*s_t, [F, D]
