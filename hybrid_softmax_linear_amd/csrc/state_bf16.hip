@@ -9,21 +9,183 @@ namespace rehyat {
 
 namespace {
 
-template <int F>
-__global__ void __launch_bounds__(256)
-state_partial_bf16_kernel(StateArgs a) {
-  // W^T [F][128] (K-tile layout) + one K tile + one V^T tile
-  __shared__ __attribute__((aligned(16))) unsigned char wt[F * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char kt[kKTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[kVTileBytes];
+// Per-segment partials, one segment per workgroup of 4 waves, two workgroups per CU. The
+// kernel is bound by HBM latency, so tiles of 32 rows stream into four LDS stages by
+// direct-to-LDS loads (three in flight while one is reduced) and the W^T operand stays in
+// registers. The operand values and the order of every MFMA chain are those of
+// segment_partial (partial_bf16.h): the results are the same bits.
+constexpr int kBufWord3 = 0x00020000;         // gfx9 buffer descriptor word 3 (raw, 32-bit data)
+constexpr int kPRows = 32;                    // rows per tile
+constexpr int kPStages = 4;
+constexpr int kPKRow = 272;                   // K row: 256 B + 16 B pad (17 slots of 16 B)
+constexpr int kPVRow = 288;                   // V row: 256 B + 32 B pad (18 slots)
+constexpr int kPInsts = 9;                    // 1 KB DMA instructions per tile and tensor
+constexpr int kPRegion = kPInsts * 1024;      // 9 KB each for K and V
+constexpr int kPStage = 2 * kPRegion;         // 18 KB
 
-  const int tid = threadIdx.x;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until this wave's loads of all but its `pending` latest tiles have landed: waves 0, 1
+// issue 5 of a tile's 18 instructions, waves 2, 3 issue 4.
+__device__ __forceinline__ void wait_tiles(int pending, int wave) {
+  if (wave < 2) {
+    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
+    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  } else {
+    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+}
+
+// two workgroups per CU; F = 256 (two feature blocks per wave) needs the registers of one
+constexpr int partial_min_blocks(int F) { return F > 128 ? 1 : 2; }
+
+template <int F>
+__global__ void __launch_bounds__(256, partial_min_blocks(F))
+state_partial_bf16_kernel(StateArgs a) {
+  // four tile stages; W^T is staged in their space first and read into registers
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStage];
+  static_assert(F * 256 <= kPStages * kPStage, "W^T staging exceeds the tile stages");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = blockIdx.x % a.n_seg;
   const int bh = blockIdx.x / a.n_seg;
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.Wk) +
                       (a.w_per_head ? (int64_t)(bh % a.H) * kDim * F : 0);
-  stage_wt(wt, W, F, 0, F, tid);
-  segment_partial<F>(a, bh, seg, segment_tiles(a, seg), wt, kt, vt, tid);
+  stage_wt(smem, W, F, 0, F, tid);
+  __syncthreads();
+  constexpr int PW = FBlocks<F>::per_wave;
+  const bool active = wave < FBlocks<F>::total;
+  bf16x8 wf[PW][8];   // B operand of U = K W: W^T rows 32 fb + l % 32, d = 16 s + 8 (l / 32) ..
+#pragma unroll
+  for (int p = 0; p < PW; ++p)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      wf[p][s] = as_bf16x8(lds_read16(smem, ktile_off(32 * (wave + 4 * p) + (lane & 31),
+                                                      2 * s + (lane >> 5))));
+  __syncthreads();   // the stages may now overwrite W^T
+
+  // this segment's rows: wholly in segment A or wholly in segment B (the host's layout)
+  const int64_t r0 = (int64_t)seg * a.seg_len;
+  const int nrows = segment_rows(a, seg);
+  const bool in_a = r0 < a.na;
+  const int64_t row0 = in_a ? head_off(bh, a.a_rows, kDim) + (a.a_row0 + r0) * kDim
+                            : head_off(bh, a.b_rows, kDim) + (a.b_row0 + r0 - a.na) * kDim;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const uint16_t*>(in_a ? a.ka : a.kb) + row0), (short)0,
+      nrows * 256, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const uint16_t*>(in_a ? a.va : a.vb) + row0), (short)0,
+      nrows * 256, kBufWord3);
+  const int ntiles = (nrows + kPRows - 1) / kPRows;
+  // tile t into stage t % 4: K slot u of the 9 KB region holds row u / 17, chunk u % 17 (the
+  // pad slot copies chunk 0; slots past 32 rows hold rows of the next tile, unused); V slot u
+  // holds row u / 18, chunk u % 18 (pad slots 16, 17 copy chunk 0). Rows past the segment
+  // come back as zeros.
+  auto issue = [&](int t) {
+    unsigned char* st = smem + (t % kPStages) * kPStage;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int j = wave + 4 * i;
+      if (j < kPInsts) {
+        const int u = 64 * j + lane;
+        const int r = u / 17;
+        int c = u - 17 * r;
+        c = c == 16 ? 0 : c;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st + j * 1024), 16,
+                                                 (t * kPRows + r) * 256 + c * 16, 0, 0, 0);
+      } else if (j < 2 * kPInsts) {
+        const int jj = j - kPInsts;
+        const int u = 64 * jj + lane;
+        const int r = u / 18;
+        int c = u - 18 * r;
+        c = c >= 16 ? 0 : c;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kPRegion + jj * 1024), 16,
+                                                 (t * kPRows + r) * 256 + c * 16, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[PW][4];
+  float zp[PW];
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    zp[p] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[p][db][i] = 0.0f;
+  }
+  for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
+  const int arow = kappa(lane & 31);
+#pragma unroll 1
+  for (int t = 0; t < ntiles; ++t) {
+    const int later = ntiles - 1 - t;           // tiles issued after t, up to two in flight
+    wait_tiles(later < 2 ? later : 2, wave);
+    __syncthreads();   // tile t landed everywhere; the stage of tile t - 1 is free
+    if (t + 3 < ntiles) issue(t + 3);
+    if (!active) continue;
+    const unsigned char* kt = smem + (t % kPStages) * kPStage;
+    const unsigned char* vt = kt + kPRegion;
+    const int key0 = t * kPRows;
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      f32x16 U;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) U[i] = 0.0f;
+      bf16x8 kf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        kf[s] = as_bf16x8(lds_read16(kt, arow * kPKRow + (2 * s + (lane >> 5)) * 16));
+#pragma unroll
+      for (int s = 0; s < 8; ++s) U = mfma32(kf[s], wf[p][s], U);
+      bf16x8 Pk[2];
+      float zsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = 8 * j + 2 * e;
+          const int key = key0 + cidx(i0, lane);
+          float u0 = U[i0] * a.u_scale, u1 = U[i0 + 1] * a.u_scale;
+          float p0 = (key < nrows) ? 1.0f + u0 + 0.5f * u0 * u0 : 0.0f;
+          float p1 = (key + 1 < nrows) ? 1.0f + u1 + 0.5f * u1 * u1 : 0.0f;
+          unsigned w = pack_bf16_u32(p0, p1);
+          zsum += bf16_lo(w) + bf16_hi(w);
+          pk[e] = w;
+        }
+        Pk[j] = as_bf16x8(pk);
+      }
+      zp[p] += zsum;
+      bf16x8 vf[4][2];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) vf[db][j] = frag_tr(vt, kPVRow, 16 * j, 32 * db, lane);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[p][db] = mfma32(Pk[j], vf[db][j], acc[p][db]);
+    }
+  }
+  if (!active) return;
+  const int E = F * kDim + F;
+  float* out = a.part + ((int64_t)bh * a.n_seg + seg) * E;
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    const int fb = wave + 4 * p;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out[(int64_t)(32 * fb + crow(i, lane)) * kDim + d] = acc[p][db][i];
+    }
+    const float zf = pair_sum(zp[p]);
+    if (lane < 32) out[F * kDim + 32 * fb + lane] = zf;
+  }
 }
 
 // phi(x) for rows of x: U = X W on MFMA, phi = 1 + u + u^2/2, stored as bf16 or fp32.
@@ -320,7 +482,6 @@ template <int F, int HID> struct MlpShape {
 };
 constexpr int mlp_threads(int F, int HID) { return 256; }
 constexpr int kMlpRow = 2 * kDim + 16;   // bytes per staged row: 128 bf16 + 16 bytes of pad
-constexpr int kBufWord3 = 0x00020000;    // gfx9 buffer descriptor word 3 (raw, 32-bit data)
 constexpr int kComputeUnits = 256;       // MI355X: one workgroup of the learned map per CU
 
 template <int F, int HID>
