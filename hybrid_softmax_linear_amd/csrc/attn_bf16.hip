@@ -761,9 +761,10 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 // branch from the carried S, z), one fold workgroup per head and, in the last workgroup of
 // each head to finish, the update of S and z.
 //   * The fold workgroup forms the per-frame partial sums of the window rows that no later
-//     window reaches, two frames at a time (one per half of the workgroup, the state
-//     kernel's own arithmetic), and adds them onto S, z in frame order, exactly as the fold
-//     kernel does, into a workspace copy xs. It also writes the chunk's last To frames to
+//     window reaches, two frames at a time (one per half of the workgroup; at F = 256 one
+//     frame split over the halves) with the state kernel's operand values and MFMA order,
+//     and adds them onto S, z in frame order, exactly as the fold kernel does, into a
+//     workspace copy xs. It also writes the chunk's last To frames to
 //     the new tail, a buffer apart from the carried one.
 //   * Every workgroup of a head reports to the head's counter (a device-scope atomic) once
 //     its reads of S, z and the carried tail have returned; the one that completes the
@@ -777,7 +778,7 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 // The fold workgroup of head bh: xs = ((S + p_0) + p_1) + ... over the nseg frames (S taken
 // as 0 for the first chunk), then the new tail. Each round the two halves of the workgroup
 // form two frames' partials (F <= 128) or the two halves of one frame's (F = 256, whose
-// four feature blocks per wave would not fit beside the attention code's registers) and
+// two feature blocks per wave would not fit beside the attention code's registers) and
 // store them (pp: [2][F*D + F]); then all threads add them on elementwise, in frame order.
 template <int F>
 __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned char* smem, int tid) {
