@@ -248,3 +248,39 @@ def test_causality_and_determinism():
     assert torch.equal(y[:, :, :Np], y2[:, :, :Np])
     yb = ta.hybrid_fwd(d["q"], d["k"], d["v"], d["W"], HW=HW, Tc=Tc, To=To, causal=False)
     assert torch.equal(yb[:, :, -Np:], y[:, :, -Np:])
+
+
+def test_overflow_fallback_outlier_key():
+    """A key whose logit for one query exceeds the first window block's maximum by far more
+    than 127 (log2 units) overflows the fixed-reference accumulation; the workgroup must
+    recompute with the exact row maximum. Whole-sequence form against the oracle, and the
+    multi-launch and single-launch recurrent forms bit for bit against it (the outlier sits
+    in chunk 1, whose window spans the carried tail and the chunk)."""
+    B, H, T, HW, F, Tc, To = 1, 2, 6, 64, 128, 2, 1
+    inp = syn.make_custom(B, H, T * HW, 128, F, seed=21, dtype="bf16", HW=HW)
+    Np = Tc * HW
+    qi = Np + 5                       # a query of chunk 1
+    kj = 2 * Np - 3                   # a late key of chunk 1's window (not in its first block)
+    for h in range(H):
+        inp["k"][0, h, kj] = (inp["q"][0, h, qi].float() * 13.0).to(torch.bfloat16)
+    q, k = to_f64(inp["q"][0, 0]), to_f64(inp["k"][0, 0])
+    logit = q[qi] @ k[kj] / math.sqrt(128)
+    lo = Np - To * HW
+    block0 = (q[qi] @ k[lo:lo + 32].T / math.sqrt(128)).max()
+    assert (logit - block0) * math.log2(math.e) > 160     # far past the fp32 range of 2^x
+    d = {n: t.to(DEV) for n, t in inp.items()}
+    whole = ta.hybrid_fwd(d["q"], d["k"], d["v"], d["W"], HW=HW, Tc=Tc, To=To, causal=True)
+    torch.cuda.synchronize()
+    y = whole.double().cpu().numpy()
+    assert np.isfinite(y).all()
+    ref = pu.oracle_rows(inp, HW=HW, Tc=Tc, To=To, causal=True)
+    err = float(np.abs(y - ref).max())
+    print(f"[outlier key] max-abs vs oracle {err:.3e}; y[qi] vs v[kj] "
+          f"{float(np.abs(y[0, 0, qi] - to_f64(inp['v'][0, 0, kj])).max()):.3e}", flush=True)
+    assert err <= pu.bf16_internal_bar(inp["v"].float().abs().max().item(), ref, False)
+    for fused in (False, True):
+        rec = ta.Recurrent(B, H, 128, F, T=T, HW=HW, Tc=Tc, To=To, fused=fused)
+        outs = [rec.step(*(d[n][:, :, t * Np:(t + 1) * Np].contiguous() for n in ("q", "k", "v")),
+                         d["W"]) for t in range(T // Tc)]
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(outs, dim=2), whole), f"fused={fused}"
