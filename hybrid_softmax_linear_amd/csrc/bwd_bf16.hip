@@ -378,17 +378,32 @@ bwd_dq_kernel(BwdArgs a) {
     const unsigned char* bV = sV + buf * 2 * kKeyTile * kRowB;
     buf ^= 1;
     if (!active) continue;
-#pragma unroll 1
-    for (int kb = 0; kb < kKeyTile / 32; ++kb) {
-      if (k0 + 32 * kb >= nk) break;
-      f32x16 St, Pt;
+    // both 32-key blocks of the tile: their S and dP MFMAs first, then each block's ds and
+    // dq MFMAs (keys past nk have zero K and V rows and are masked out of ds)
+    f32x16 St[kKeyTile / 32], Pt[kKeyTile / 32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) St[i] = Pt[i] = 0.0f;
+    for (int kb = 0; kb < kKeyTile / 32; ++kb) {
+      bf16x8 kf[8], vf[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        St = mfma32(as_bf16x8(lds_read16(bK, ab + kb * 32 * kRowB + 32 * s)), Qf[s], St);
-        Pt = mfma32(as_bf16x8(lds_read16(bV, ab + kb * 32 * kRowB + 32 * s)), DYf[s], Pt);
+        kf[s] = as_bf16x8(lds_read16(bK, ab + kb * 32 * kRowB + 32 * s));
+        vf[s] = as_bf16x8(lds_read16(bV, ab + kb * 32 * kRowB + 32 * s));
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) St[kb][i] = Pt[kb][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        St[kb] = mfma32(kf[s], Qf[s], St[kb]);
+        Pt[kb] = mfma32(vf[s], DYf[s], Pt[kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKeyTile / 32; ++kb) {
+      bf16x8 kt[4][2];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) kt[db][j] = frag_tr(bK, kRowB, 32 * kb + 16 * j, 32 * db, lane);
       bf16x8 dsb[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -400,8 +415,8 @@ bwd_dq_kernel(BwdArgs a) {
           for (int q2 = 0; q2 < 2; ++q2) {
             const int i = 8 * j + 2 * e + q2;
             const int key = k0 + 32 * kb + cidx(i, lane);
-            const float p = key < nk ? fast_exp2(St[i] * ls - lse_l) : 0.0f;
-            d2[q2] = p * (Pt[i] - dd_l) * us;
+            const float p = key < nk ? fast_exp2(St[kb][i] * ls - lse_l) : 0.0f;
+            d2[q2] = p * (Pt[kb][i] - dd_l) * us;
           }
           pk[e] = pack_bf16_u32(d2[0], d2[1]);
         }
@@ -410,8 +425,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          dQ[db] = mfma32(frag_tr(bK, kRowB, 32 * kb + 16 * j, 32 * db, lane), dsb[j], dQ[db]);
+        for (int j = 0; j < 2; ++j) dQ[db] = mfma32(kt[db][j], dsb[j], dQ[db]);
     }
   }
   if (ok) {
