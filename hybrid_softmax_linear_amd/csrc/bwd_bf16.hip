@@ -16,7 +16,8 @@
 //   map:     gx = dphi (1 + u) / sqrt(D),  dx += W gx,  dW += sum_rows x gx^T.
 // den comes from the forward as lse = log2(den). MFMA operands follow the conventions of
 // common.h (C tiles of a first product taken in the kappa row order feed the next product
-// directly); LDS rows of 128 bf16 are padded to 272 bytes.
+// directly). The window parts' tiles are stored in bank-conflict-free swizzled layouts
+// (Swz320, Swz256 below); the linear parts' slabs in rows of 128 bf16 padded to 272 bytes.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -31,27 +32,78 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
-// Direct-to-LDS copy of `rows` rows of 256 B (row r at byte r*256 of the buffer) into LDS
-// rows of 272 B. Instruction j writes the 64 consecutive 16-byte slots 64j..64j+63; slot u
-// is row u/17, chunk u%17 (chunk 16, the pad, takes a copy of chunk 0). Rows past the
-// buffer's range read as zeros.
-template <int ROWS, int NW>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t src, unsigned char* dst, int wave,
+// Operand tiles of the window parts. Their rows (128 bf16: one query, key or value each)
+// are read two ways: as 16-byte A-operand pieces, 16 rows (in kappa order) at one chunk per
+// 16 lanes, which LDS serves in one 256-byte pass; and by the transposing read, whose 32
+// lanes of a pass touch 4 consecutive rows x 64 bytes. No padded row stride alone keeps
+// both on 64 distinct banks (272 B serves the first and costs the second four passes), so
+// chunk c (16 bytes) of row r is stored at chunk c ^ h(r mod 16) of the row:
+//   Swz320: rows of 320 B (80 words, 16 mod 64; slots 16..19 are pad), h = (r / 4) mod 4;
+//   Swz256: rows of 256 B, h = (r ^ 4r) mod 16.
+// Either way every pass of both reads hits 64 distinct banks. a_off and t_off are the byte
+// offsets of a lane's pieces within a block of 32 (A pieces) or 16 (transposing reads) rows;
+// they are written so that few distinct per-lane bases remain (the rest are immediates):
+// Swz320's h leaves chunk bits 2, 3 alone (2 + 2 bases); in Swz256 row r + 4 has h ^ 4, so the
+// second transposing read of a fragment is the first one's of column block db ^ 1, four rows
+// down (8 + 4 bases). The 256-byte form is for the tile pairs that do not fit at 320 B.
+struct Swz320 {
+  static constexpr int kRow = 320, kSlots = 20;
+  __device__ static int h(int r) { return (r >> 2) & 3; }
+  // A piece s (chunk 2s + l/32) of row kappa(l mod 32)
+  __device__ static int a_off(int lane, int s) {
+    const int r = kappa(lane & 31);
+    return r * kRow + 16 * ((2 * (s & 1) + (lane >> 5)) ^ h(r)) + 64 * (s >> 1);
+  }
+  // transposing read hi (rows 4 hi .. 4 hi + 3 of each 8) of columns 32 db .. 32 db + 31
+  __device__ static int t_off(int lane, int db, int hi) {
+    const int g = lane >> 4, q = lane & 15;
+    const int r = 8 * (g >> 1) + (q >> 2) + 4 * hi;
+    return r * kRow + 16 * ((2 * (g & 1) + ((q & 3) >> 1)) ^ h(r)) + 8 * (q & 1) + 64 * db;
+  }
+};
+struct Swz256 {
+  static constexpr int kRow = 256, kSlots = 16;
+  __device__ static int h(int r) { return (r ^ (r << 2)) & 15; }
+  __device__ static int a_off(int lane, int s) {
+    const int r = kappa(lane & 31);
+    return r * kRow + 16 * ((2 * s + (lane >> 5)) ^ h(r));
+  }
+  __device__ static int t_off(int lane, int db, int hi) {
+    const int g = lane >> 4, q = lane & 15;
+    const int r = 8 * (g >> 1) + (q >> 2);
+    const int d = hi ? db ^ 1 : db;
+    return (r + 4 * hi) * kRow + 16 * ((4 * d + 2 * (g & 1) + ((q & 3) >> 1)) ^ h(r)) + 8 * (q & 1);
+  }
+};
+
+// Direct-to-LDS copy of ROWS rows of 256 B (row r at byte r*256 of the buffer) into a tile
+// of layout L. Instruction j writes the 64 consecutive 16-byte slots 64j..64j+63; slot u is
+// row u / kSlots, stored chunk p = u mod kSlots, which holds chunk p ^ h(row) (pad slots
+// take a copy of chunk 0). Rows past the buffer's range read as zeros.
+template <class L, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t src, unsigned char* dst, int wave,
                                          int lane) {
-  constexpr int kInsts = ROWS * 17 / 64;
-  static_assert(ROWS * 17 % 64 == 0, "whole DMA instructions");
+  constexpr int kInsts = ROWS * L::kSlots / 64;
+  static_assert(ROWS * L::kSlots % 64 == 0, "whole DMA instructions");
 #pragma unroll
   for (int i = 0; i < (kInsts + NW - 1) / NW; ++i) {
     const int j = wave + NW * i;
     if (j < kInsts) {
       const int u = 64 * j + lane;
-      const int r = u / 17;
-      int c = u - 17 * r;
-      c = c == 16 ? 0 : c;
+      const int r = u / L::kSlots;
+      const int p = u - L::kSlots * r;
+      const int c = p < 16 ? p ^ L::h(r & 15) : 0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(dst + j * 1024), 16,
                                                r * 256 + c * 16, 0, 0, 0);
     }
   }
+}
+
+// Transposing fragment of a layout-L tile: the two reads at lo and hi (t_off(.., 0 / 1)).
+__device__ __forceinline__ bf16x8 frag_tr_at(const unsigned char* lo, const unsigned char* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Plain staging of `rows` rows of `cols` bf16 (row stride ld elements, from column c0) into
@@ -201,7 +253,8 @@ dw_finalize_kernel(const float* __restrict__ parts, int64_t E, int BH, int H, in
 constexpr int kQW = 8;                                   // waves of the dq kernel
 constexpr int kLinLds = 3 * 128 * kRowB;                 // W^T, S and W slabs
 constexpr int kKeyTile = 64;
-constexpr int kDqLds = kLinLds > 4 * kKeyTile * kRowB ? kLinLds : 4 * kKeyTile * kRowB;
+using KL = Swz320;                                       // layout of the K and V tiles
+constexpr int kDqLds = kLinLds > 4 * kKeyTile * KL::kRow ? kLinLds : 4 * kKeyTile * KL::kRow;
 
 struct BwdGeo {
   int bh, t;
@@ -237,7 +290,9 @@ bwd_dq_kernel(BwdArgs a) {
   constexpr int RW = 2 * FS + 16;                        // bytes per W slab row
   __shared__ __attribute__((aligned(16))) unsigned char smem[kDqLds];
   __shared__ float zs[F];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: held in a scalar register, the tile loads' LDS addresses are
+  // scalar too and free vector registers for the loop
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int qt;
   const BwdGeo g = bwd_geo(a, blockIdx.x, qt);
   const int qw0 = qt * 256 + wave * 32;                  // first query of the wave in the chunk
@@ -353,9 +408,8 @@ bwd_dq_kernel(BwdArgs a) {
   const int nk = (int)(g.hi - g.lo);
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (hrow + g.lo) * kDim;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + (hrow + g.lo) * kDim;
-  unsigned char* sK = smem;                      // buffer b: K tile at sK + b * 2 * kKeyTile * kRowB
-  unsigned char* sV = smem + kKeyTile * kRowB;   //           V tile right after it
-  const int ab = kappa(lane & 31) * kRowB + 16 * (lane >> 5);
+  unsigned char* sK = smem;                          // buffer b: K tile at sK + b * 2 * kKeyTile * KL::kRow
+  unsigned char* sV = smem + kKeyTile * KL::kRow;    //           V tile right after it
   const float ls = a.logit_scale;
   auto issue = [&](int k0, int buf) {
     const int bytes = (nk - k0) * 256;
@@ -363,8 +417,8 @@ bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * kDim), (short)0, bytes, kBufWord3);
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * kDim), (short)0, bytes, kBufWord3);
-    dma_rows<kKeyTile, kQW>(kr, sK + buf * 2 * kKeyTile * kRowB, wave, lane);
-    dma_rows<kKeyTile, kQW>(vr, sV + buf * 2 * kKeyTile * kRowB, wave, lane);
+    dma_tile<KL, kKeyTile, kQW>(kr, sK + buf * 2 * kKeyTile * KL::kRow, wave, lane);
+    dma_tile<KL, kKeyTile, kQW>(vr, sV + buf * 2 * kKeyTile * KL::kRow, wave, lane);
   };
   __syncthreads();   // the linear part's slabs are no longer read
   issue(0, 0);
@@ -374,8 +428,8 @@ bwd_dq_kernel(BwdArgs a) {
     wait_vmem_all();
     __syncthreads();   // this tile landed everywhere; the other buffer is free
     if (k0 + kKeyTile < nk) issue(k0 + kKeyTile, buf ^ 1);
-    const unsigned char* bK = sK + buf * 2 * kKeyTile * kRowB;
-    const unsigned char* bV = sV + buf * 2 * kKeyTile * kRowB;
+    const unsigned char* bK = sK + buf * 2 * kKeyTile * KL::kRow;
+    const unsigned char* bV = sV + buf * 2 * kKeyTile * KL::kRow;
     buf ^= 1;
     if (!active) continue;
     // both 32-key blocks of the tile: their S and dP MFMAs first, then each block's ds and
@@ -386,8 +440,8 @@ bwd_dq_kernel(BwdArgs a) {
       bf16x8 kf[8], vf[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        kf[s] = as_bf16x8(lds_read16(bK, ab + kb * 32 * kRowB + 32 * s));
-        vf[s] = as_bf16x8(lds_read16(bV, ab + kb * 32 * kRowB + 32 * s));
+        kf[s] = as_bf16x8(lds_read16(bK, KL::a_off(lane, s) + kb * 32 * KL::kRow));
+        vf[s] = as_bf16x8(lds_read16(bV, KL::a_off(lane, s) + kb * 32 * KL::kRow));
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) St[kb][i] = Pt[kb][i] = 0.0f;
@@ -403,7 +457,10 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) kt[db][j] = frag_tr(bK, kRowB, 32 * kb + 16 * j, 32 * db, lane);
+        for (int j = 0; j < 2; ++j) {
+          const unsigned char* t = bK + (32 * kb + 16 * j) * KL::kRow;
+          kt[db][j] = frag_tr_at(t + KL::t_off(lane, db, 0), t + KL::t_off(lane, db, 1));
+        }
       bf16x8 dsb[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -456,7 +513,8 @@ bwd_dq_kernel(BwdArgs a) {
 // lies in that frame.
 constexpr int kKW = 4;                                    // waves of the dk/dv kernel
 constexpr int kQTile = 128;
-constexpr int kQBuf = 2 * kQTile * kRowB + 2 * kQTile * 4;   // Q, dY rows; lse, dy.y
+using QL = Swz256;                                        // layout of the Q and dY tiles
+constexpr int kQBuf = 2 * kQTile * QL::kRow + 2 * kQTile * 4;   // Q, dY rows; lse, dy.y
 constexpr int kDkLds = kLinLds > 2 * kQBuf ? kLinLds : 2 * kQBuf;
 
 template <int F>
@@ -466,7 +524,9 @@ bwd_dkdv_kernel(BwdArgs a) {
   constexpr int RW = 2 * FS + 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kDkLds];
   __shared__ float hs[F];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: held in a scalar register, the tile loads' LDS addresses are
+  // scalar too and free vector registers for the loop
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int kt;
   const BwdGeo g = bwd_geo(a, blockIdx.x, kt);
   const int kw0 = kt * 128 + wave * 32;                  // first key of the wave in the chunk
@@ -516,8 +576,8 @@ bwd_dkdv_kernel(BwdArgs a) {
         kBufWord3);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.dyb + (hrow + r0) * kDim), (short)0, bytes, kBufWord3);
-    dma_rows<kQTile, kKW>(qr, base, wave, lane);
-    dma_rows<kQTile, kKW>(yr, base + kQTile * kRowB, wave, lane);
+    dma_tile<QL, kQTile, kKW>(qr, base, wave, lane);
+    dma_tile<QL, kQTile, kKW>(yr, base + kQTile * QL::kRow, wave, lane);
     // lse and dy.y of the tile: 4 bytes per lane, one instruction per 64 rows each
     const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.lse + hrow + r0), (short)0, bytes / 64, kBufWord3);
@@ -525,9 +585,9 @@ bwd_dkdv_kernel(BwdArgs a) {
         (void*)(a.dvec + hrow + r0), (short)0, bytes / 64, kBufWord3);
     if (wave < kQTile / 64) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          lr, (lds_void*)(base + 2 * kQTile * kRowB + wave * 256), 4, (wave * 64 + lane) * 4, 0, 0, 0);
+          lr, (lds_void*)(base + 2 * kQTile * QL::kRow + wave * 256), 4, (wave * 64 + lane) * 4, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          dr, (lds_void*)(base + 2 * kQTile * kRowB + kQTile * 4 + wave * 256), 4,
+          dr, (lds_void*)(base + 2 * kQTile * QL::kRow + kQTile * 4 + wave * 256), 4,
           (wave * 64 + lane) * 4, 0, 0, 0);
     }
   };
@@ -546,8 +606,8 @@ bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();   // tile landed everywhere; the other buffer's last reader is done
     if (nhave) issue(ntq, nq0, qbuf ^ 1);
     const unsigned char* sQ = smem + qbuf * kQBuf;
-    const unsigned char* sY = sQ + kQTile * kRowB;
-    const float* sL = reinterpret_cast<const float*>(sQ + 2 * kQTile * kRowB);
+    const unsigned char* sY = sQ + kQTile * QL::kRow;
+    const float* sL = reinterpret_cast<const float*>(sQ + 2 * kQTile * QL::kRow);
     const float* sD = sL + kQTile;
     const bool key_in = ok && key >= chunk_lo(tq);
     tq = ntq;
@@ -567,8 +627,8 @@ bwd_dkdv_kernel(BwdArgs a) {
         bf16x8 qf[8], yf[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          qf[s] = as_bf16x8(lds_read16(sQ, ab + qb * 32 * kRowB + 32 * s));
-          yf[s] = as_bf16x8(lds_read16(sY, ab + qb * 32 * kRowB + 32 * s));
+          qf[s] = as_bf16x8(lds_read16(sQ, QL::a_off(lane, s) + qb * 32 * QL::kRow));
+          yf[s] = as_bf16x8(lds_read16(sY, QL::a_off(lane, s) + qb * 32 * QL::kRow));
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[h2][i] = Pd[h2][i] = 0.0f;
@@ -595,8 +655,9 @@ bwd_dkdv_kernel(BwdArgs a) {
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            yt[db][j] = frag_tr(sY, kRowB, 32 * qb + 16 * j, 32 * db, lane);
-            qt[db][j] = frag_tr(sQ, kRowB, 32 * qb + 16 * j, 32 * db, lane);
+            const int o = (32 * qb + 16 * j) * QL::kRow;
+            yt[db][j] = frag_tr_at(sY + o + QL::t_off(lane, db, 0), sY + o + QL::t_off(lane, db, 1));
+            qt[db][j] = frag_tr_at(sQ + o + QL::t_off(lane, db, 0), sQ + o + QL::t_off(lane, db, 1));
           }
         bf16x8 pb[2], dsb[2];
 #pragma unroll
