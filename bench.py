@@ -295,10 +295,36 @@ def cpu_baseline(inp, cfg):
             "sample": f"{workers} of {heads_total} heads of the same workload (all {cfg.N} query "
                       f"rows each), one head per process, 1 BLAS thread each; wall {wall:.1f} s, "
                       f"mean {sum(per_head) / len(per_head):.1f} s per head; scaled to all heads",
-            "host_cores_visible": cores}
+            "host_cores_visible": cores, "cpu_model": _cpu_model(), "blas_threads": 1}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ---- GPU timing -----------------------------------------------------------------------
+
+def step_distribution(fn, n):
+    """Median, p10 and p90 of n individually timed calls (events around each call)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    return {"n": n, "median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9)}
+
 
 def time_calls(fn, steps, warmup):
     import torch
@@ -457,6 +483,8 @@ def main(argv=None):
     kern_ms, launches = hs.rehyat_timing_read()
     hs.rehyat_timing_enable(False)
     kern_avg = kern_ms / max(launches, 1)
+    # after the timed region: the spread of single steps
+    dist = step_distribution(step, 50)
 
     total_flop, attn_flop, state_flop, pairs = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D,
                                                           desc.F, cfg.Tc, cfg.To, causal=True,
@@ -551,6 +579,7 @@ def main(argv=None):
         "tflops": tflops,
         "mfma_peak_frac": tflops / MFMA_PEAK_BF16_TFLOPS,
         "flop_per_step": total_flop,
+        "step_ms_distribution": dist,
         "roofline": {"bound": "mfma", "kernel": "hybrid_attn_bf16_kernel<128>",
                      "achieved": attn_tflops, "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
