@@ -11,8 +11,9 @@ namespace {
 
 // Per-segment partials, one segment per workgroup of 4 waves, two workgroups per CU. The
 // kernel is bound by HBM latency, so tiles of 32 rows stream into four LDS stages by
-// direct-to-LDS loads (three in flight while one is reduced) and the W^T operand stays in
-// registers. The operand values and the order of every MFMA chain are those of
+// direct-to-LDS loads (up to three in flight while one is reduced; each tile's loads are
+// issued after the previous tile's transposing reads, which wait for all loads in flight)
+// and the W^T operand stays in registers. The operand values and the order of every MFMA chain are those of
 // segment_partial (partial_bf16.h): the results are the same bits.
 constexpr int kBufWord3 = 0x00020000;         // gfx9 buffer descriptor word 3 (raw, 32-bit data)
 constexpr int kPRows = 32;                    // rows per tile
@@ -125,8 +126,10 @@ state_partial_bf16_kernel(StateArgs a) {
     const int later = ntiles - 1 - t;           // tiles issued after t, up to two in flight
     wait_tiles(later < 2 ? later : 2, wave);
     __syncthreads();   // tile t landed everywhere; the stage of tile t - 1 is free
-    if (t + 3 < ntiles) issue(t + 3);
-    if (!active) continue;
+    if (!active) {
+      if (t + 3 < ntiles) issue(t + 3);
+      continue;
+    }
     const unsigned char* kt = smem + (t % kPStages) * kPStage;
     const unsigned char* vt = kt + kPRegion;
     const int key0 = t * kPRows;
@@ -165,6 +168,9 @@ state_partial_bf16_kernel(StateArgs a) {
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int j = 0; j < 2; ++j) vf[db][j] = frag_tr(vt, kPVRow, 16 * j, 32 * db, lane);
+      // tile t + 3 goes out only now: the compiler makes a transposing LDS read wait for
+      // every load in flight, so loads issued before these reads would be waited for here
+      if (p == 0 && t + 3 < ntiles) issue(t + 3);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
