@@ -10,7 +10,6 @@ from .rehyat_oracle import (  # noqa: F401
     chunk_layout,
     phi,
     hybrid_attention,
-    hybrid_attention_bh,
     hybrid_recurrent,
     state_direct,
     recurrent_init,

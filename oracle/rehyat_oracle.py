@@ -55,7 +55,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "chunk_layout", "phi", "hybrid_attention", "hybrid_attention_bh", "hybrid_recurrent",
+    "chunk_layout", "phi", "hybrid_attention", "hybrid_recurrent",
     "state_direct", "recurrent_init", "recurrent_step", "EluFeatureMap", "PolyMlpFeatureMap",
     "feature", "feature_dim", "hybrid_attention_bwd",
 ]
@@ -196,49 +196,6 @@ def hybrid_attention(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool
             nL_out[pos] = nL
     if return_stats:
         return y, {"nS": nS_out, "nL": nL_out}
-    return y
-
-
-def _w_for_head(W, h: int):
-    if callable(W):
-        return W
-    if isinstance(W, (list, tuple)):
-        return W[h]
-    W = np.asarray(W)
-    return W if W.ndim == 2 else W[h]
-
-
-def _one_head(args):
-    (q, k, v, Wq, Wk, HW, Tc, To, causal, rows, block) = args
-    return hybrid_attention(q, k, v, Wq, Wk, HW=HW, Tc=Tc, To=To, causal=causal,
-                            rows=rows, block=block)
-
-
-def hybrid_attention_bh(q, k, v, Wq, Wk, *, HW: int, Tc: int, To: int, causal: bool = True,
-                        rows: Optional[Sequence[int]] = None, block: int = 256,
-                        processes: int = 1, heads: Optional[Sequence[Tuple[int, int]]] = None):
-    """hybrid_attention over [B, H, N, D] inputs; W is [D, F] (shared) or [H, D, F].
-
-    heads: optional list of (b, h) pairs to evaluate (others are left as NaN).
-    processes > 1 evaluates heads in a process pool (one BLAS thread per process is the
-    caller's business: set OMP_NUM_THREADS / OPENBLAS_NUM_THREADS before numpy loads).
-    Returns y [B, H, len(rows) or N, Dv].
-    """
-    B, H, N, _ = q.shape
-    nrows = N if rows is None else len(rows)
-    y = np.full((B, H, nrows, v.shape[-1]), np.nan)
-    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
-    jobs = [(q[b, h], k[b, h], v[b, h], _w_for_head(Wq, h), _w_for_head(Wk, h),
-             HW, Tc, To, causal, rows, block) for (b, h) in pairs]
-    if processes > 1 and len(jobs) > 1:
-        import multiprocessing as mp
-        ctx = mp.get_context("fork")
-        with ctx.Pool(processes) as pool:
-            outs = pool.map(_one_head, jobs)
-    else:
-        outs = [_one_head(j) for j in jobs]
-    for (b, h), o in zip(pairs, outs):
-        y[b, h] = o
     return y
 
 
