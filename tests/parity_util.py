@@ -4,19 +4,13 @@ summaries and the tolerance model.
 Tolerances
   * fp32 path: max-abs error <= 1e-4 (the required bar for fp32).
   * bf16 path: max-abs error <= 3e-2 (the required bar for bf16 inputs, fp32 accumulation).
-    Internal bar, derived from where the kernel rounds: the softmax weights p_j enter the
-    PV product as bf16 (relative error <= 2^-9 each), phi(q) and the state S enter the
-    linear read-out as bf16 (<= 2^-9 each). y is a weighted mean of values with positive
-    weights, and perturbing each weight by a factor (1+d_j), |d_j| <= 2^-9, moves a
-    weighted mean by at most 2^-9 * max_j |v_j - y| / (1 - 2^-9) <= 2^-8 * max|v| (both
-    numerator and denominator use the same rounded weights). The linear branch adds the
-    same order again. Hence |err| <= 2 * 2^-8 * max|v| (+ 2^-9 * max|y| when y is stored
-    as bf16). Typical errors are an order of magnitude below this bound; per-chunk errors
-    are reported by every test.
   * bf16 path, per chunk: max-abs error <= 2^-7 * max|y| over that chunk's rows (+ 2^-9 for
-    bf16 y). The worst-case bound above is loose because the rounding errors of thousands
-    of weights average out: to first order the error of a row is sum_j w_j d_j (v_j - y) /
-    sum_j w_j with independent d_j, |d_j| <= 2^-9. Emulating the kernel's roundings on the
+    bf16 y). This is the bar that discriminates. A worst-case bound from the rounding points
+    (p, phi(q) and S each enter an MFMA as bf16, a relative error <= 2^-9 per weight of a
+    weighted mean) gives 2 * 2^-8 * max|v|, which at the full workloads (max|v| up to 9)
+    lies above the 3e-2 bar and so checks nothing; it is not asserted. The rounding errors
+    of thousands of weights average out instead: to first order the error of a row is
+    sum_j w_j d_j (v_j - y) / sum_j w_j with independent d_j, |d_j| <= 2^-9. Emulating the kernel's roundings on the
     full workloads in float64 gives at most 1.5e-3 * max|y| per chunk, while leaving out
     the overlap frames, folding the overlap into the state (the unamended recurrence),
     folding one frame too few, or dropping the softmax branch moves y by 1.5e-2 to 1.0 of
@@ -40,15 +34,6 @@ BF16_BAR = 3e-2
 CHUNK_REL_BAR = 2.0 ** -7
 
 
-def bf16_internal_bar(v, y_ref: np.ndarray, y_bf16: bool) -> float:
-    """v: the values (array or tensor) or their max-abs as a float."""
-    vmax = float(v) if np.isscalar(v) else float(np.abs(np.asarray(v)).max())
-    bar = 2.0 * 2.0 ** -8 * vmax
-    if y_bf16:
-        bar += 2.0 ** -9 * float(np.abs(y_ref).max())
-    return bar
-
-
 def chunk_rel_bar(y_bf16: bool) -> float:
     return CHUNK_REL_BAR + (2.0 ** -9 if y_bf16 else 0.0)
 
@@ -56,6 +41,16 @@ def chunk_rel_bar(y_bf16: bool) -> float:
 def chunk_rel_errors(errs: List[Dict[str, float]]) -> List[float]:
     """Per-chunk max-abs error in units of that chunk's max|y|."""
     return [e["max_abs"] / max(e["max_ref"], 1e-30) for e in errs]
+
+
+def assert_bf16(errs: List[Dict[str, float]], y_bf16: bool, cond: float = 1.0) -> None:
+    """The bf16 bars: max-abs <= 3e-2 overall and, per chunk, max-abs <= cond * (2^-7 (+ 2^-9
+    for bf16 y)) * that chunk's max|y| (cond: the conditioning factor of signed weights, 1
+    for one-signed weights)."""
+    err = max(e["max_abs"] for e in errs)
+    assert err <= BF16_BAR, f"max-abs {err:.3e} > {BF16_BAR}"
+    rel = chunk_rel_errors(errs)
+    assert max(rel) <= cond * chunk_rel_bar(y_bf16), f"per-chunk relative errors {rel}"
 
 
 def oracle_rows(inp: Dict[str, torch.Tensor], *, HW: int, Tc: int, To: int, causal: bool,

@@ -61,10 +61,7 @@ def _check(y, ref, inp, *, bf16, y_bf16, T, HW, Tc, rows=None, label=""):
           flush=True)
     assert np.isfinite(y).all()
     if bf16:
-        assert err <= pu.BF16_BAR, f"max-abs {err:.3e} > {pu.BF16_BAR}"
-        bar = pu.bf16_internal_bar(to_f64(inp["v"]), ref, y_bf16)
-        assert err <= bar, f"max-abs {err:.3e} > internal bar {bar:.3e}"
-        assert rel <= pu.chunk_rel_bar(y_bf16), f"per-chunk relative {rel:.3e}"
+        pu.assert_bf16(errs, y_bf16)
     else:
         assert err <= pu.F32_BAR, f"max-abs {err:.3e} > {pu.F32_BAR}"
     return err
@@ -277,7 +274,7 @@ def test_overflow_fallback_outlier_key():
     err = float(np.abs(y - ref).max())
     print(f"[outlier key] max-abs vs oracle {err:.3e}; y[qi] vs v[kj] "
           f"{float(np.abs(y[0, 0, qi] - to_f64(inp['v'][0, 0, kj])).max()):.3e}", flush=True)
-    assert err <= pu.bf16_internal_bar(inp["v"].float().abs().max().item(), ref, False)
+    pu.assert_bf16(pu.chunk_errors(y, ref, list(range(T * HW)), T, HW, Tc), False)
     for fused in (False, True):
         rec = ta.Recurrent(B, H, 128, F, T=T, HW=HW, Tc=Tc, To=To, fused=fused)
         outs = [rec.step(*(d[n][:, :, t * Np:(t + 1) * Np].contiguous() for n in ("q", "k", "v")),
