@@ -766,14 +766,18 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 //     and adds them onto S, z in frame order, exactly as the fold kernel does, into a
 //     workspace copy xs. It also writes the chunk's last To frames to
 //     the new tail, a buffer apart from the carried one.
-//   * Every workgroup of a head reports to the head's counter (a device-scope atomic) once
-//     its reads of S, z and the carried tail have returned; the one that completes the
+//   * Every workgroup of a head reports to the head's counter (an agent-scope atomic add)
+//     once its reads of S, z and the carried tail have returned; the one that completes the
 //     count is the only one left that could read S and z, and copies xs into them.
 // No workgroup waits for another. The only data that crosses workgroups inside the launch
-// is xs: the fold workgroup writes it with device-scope stores (through the XCD's L2) and
-// waits for them before it reports; the last workgroup reads it with device-scope loads.
-// (A full fence, an L2 write-back and invalidate of the XCD, in every workgroup cost more
-// than the whole fold.)
+// is xs, and it is ordered by a release/acquire pair at agent scope: the fold workgroup's
+// add is a release (after the workgroup barrier that follows its xs stores), the other
+// workgroups' relaxed adds continue its release sequence, and the last workgroup issues an
+// acquire fence after its add and before it reads xs. Only the fold workgroup and the last
+// workgroup of a head pay for the cache write-back and invalidate these imply; a release
+// in every workgroup cost more than the whole fold. The reads of S and z need no fence:
+// each workgroup consumes their values before the barrier ahead of its add, and the last
+// workgroup stores only after its add has returned the final count.
 
 // The fold workgroup of head bh: xs = ((S + p_0) + p_1) + ... over the nseg frames (S taken
 // as 0 for the first chunk), then the new tail. Each round the two halves of the workgroup
@@ -825,7 +829,6 @@ __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned ch
     }
     __syncthreads();   // the round's partials stored (workgroup scope)
     const bool pair = !kSplit && 2 * r + 1 < nseg;
-    const bool last = kPer * r + kPer >= nseg;
 #pragma unroll 1
     for (int e = 4 * tid; e < E; e += 4 * NT) {
       f32x4 x;
@@ -837,13 +840,7 @@ __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned ch
         x = *reinterpret_cast<const f32x4*>(e < F * kDim ? S0 + e : z0 + (e - F * kDim));
       x += *reinterpret_cast<const f32x4*>(pp + e);
       if (pair) x += *reinterpret_cast<const f32x4*>(pp + E + e);
-      if (last) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(xs + e + i, x[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        *reinterpret_cast<f32x4*>(xs + e) = x;
-      }
+      *reinterpret_cast<f32x4*>(xs + e) = x;
     }
     __syncthreads();   // pp free for the next round
   }
@@ -875,7 +872,6 @@ __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned ch
       }
     }
   }
-  wait_vmem();   // xs's device-scope stores have completed
 }
 
 // The last workgroup of head bh: S, z <- xs (or 0 for a first chunk with nothing folded).
@@ -889,11 +885,7 @@ __device__ __forceinline__ void finish_head(const StepArgs& s, int bh, int tid) 
   for (int e = 4 * tid; e < E; e += 4 * NT) {
     float* dst = e < F * kDim ? Sd + e : zd + (e - F * kDim);
     f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (copy) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[i] = __hip_atomic_load(xs + e + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (copy) x = *reinterpret_cast<const f32x4*>(xs + e);
     if (copy || s.init) *reinterpret_cast<f32x4*>(dst) = x;
   }
 }
@@ -919,8 +911,17 @@ recurrent_step_bf16_kernel(AttnArgs a, StepArgs s) {
     bh = attention_block<F, true, true>(a, b - s.fold_blocks, smem, zs, bad_flag);
   }
   __syncthreads();
-  if (tid == 0)
-    last_flag = atomicAdd(s.counter + bh, 1u) == (unsigned)(s.per_head - 1) ? 1 : 0;
+  if (tid == 0) {
+    // the fold workgroup releases xs (its threads' stores precede the barrier above); the
+    // last workgroup acquires it
+    const unsigned prev =
+        b < s.fold_blocks
+            ? __hip_atomic_fetch_add(s.counter + bh, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT)
+            : __hip_atomic_fetch_add(s.counter + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == (unsigned)(s.per_head - 1) ? 1 : 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    last_flag = last;
+  }
   __syncthreads();
   if (!last_flag) return;
   finish_head<F>(s, bh, tid);
