@@ -23,12 +23,14 @@ __all__ = [
     "rehyat_hybrid_fwd", "rehyat_hybrid_fwd_workspace",
     "rehyat_recurrent_step", "rehyat_recurrent_step_workspace",
     "rehyat_recurrent_step_fused", "rehyat_recurrent_step_fused_workspace",
+    "rehyat_recurrent_step_fused_noalloc", "STATIC_SCRATCH_BYTES",
     "rehyat_hybrid_fwd_stats", "rehyat_hybrid_bwd", "rehyat_hybrid_bwd_workspace",
     "rehyat_timing_enable", "rehyat_timing_read", "F32", "BF16", "CAUSAL", "BIDIR",
     "PHI_POLY2", "PHI_ELU", "PHI_MLP",
 ]
 
 F32, BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 16 * 1024 * 1024   # REHYAT_STATIC_SCRATCH_BYTES of include/rehyat.h
 CAUSAL, BIDIR = 0, 1
 PHI_POLY2, PHI_ELU, PHI_MLP = 0, 1, 2
 
@@ -103,6 +105,8 @@ _SIGS = {
                               [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
     "rehyat_recurrent_step_fused": (ctypes.c_int, [ctypes.POINTER(_CDesc), ctypes.c_int32] +
                                     [ctypes.c_void_p] * 13 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "rehyat_recurrent_step_fused_noalloc": (ctypes.c_int, [ctypes.POINTER(_CDesc), ctypes.c_int32] +
+                                            [ctypes.c_void_p] * 13),
     "rehyat_hybrid_fwd_stats": (ctypes.c_int, [ctypes.POINTER(_CDesc)] + [ctypes.c_void_p] * 8 +
                                 [ctypes.c_size_t, ctypes.c_void_p]),
     "rehyat_hybrid_bwd_workspace": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
@@ -253,6 +257,21 @@ def rehyat_recurrent_step_fused(desc: Desc, chunk_index: int, q_c, k_c, v_c, Wq,
                                              _ptr(k_tail_out), _ptr(v_tail_out), _ptr(y_c),
                                              _ptr(ws), nb, _stream(stream)),
            "rehyat_recurrent_step_fused")
+
+
+def rehyat_recurrent_step_fused_noalloc(desc: Desc, chunk_index: int, q_c, k_c, v_c, Wq, Wk,
+                                        S, z, k_tail, v_tail, k_tail_out, v_tail_out, y_c,
+                                        stream=None) -> None:
+    """rehyat_recurrent_step_fused with its scratch in the library's static device array
+    (no workspace, nothing allocated; see include/rehyat.h for the size limit and the
+    sharing rules)."""
+    _check(lib().rehyat_recurrent_step_fused_noalloc(ctypes.byref(desc.c()), int(chunk_index),
+                                                     _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(Wq),
+                                                     _ptr(Wk), _ptr(S), _ptr(z), _ptr(k_tail),
+                                                     _ptr(v_tail), _ptr(k_tail_out),
+                                                     _ptr(v_tail_out), _ptr(y_c),
+                                                     _stream(stream)),
+           "rehyat_recurrent_step_fused_noalloc")
 
 
 def rehyat_timing_enable(enable, kernel: int = 1) -> None:

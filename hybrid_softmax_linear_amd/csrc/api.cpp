@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/rehyat.h"
 #include "common.h"
@@ -490,7 +491,8 @@ int step_frames(const rehyat_desc* d, int32_t t) {
 rehyat_status check_step(const rehyat_desc* d, int32_t t, const void* q_c, const void* k_c,
                          const void* v_c, const void* Wq, const void* Wk, const float* S,
                          const float* z, const void* k_tail, const void* v_tail, const void* y_c,
-                         const void* ws, size_t ws_bytes, size_t need) {
+                         const void* ws, size_t ws_bytes, size_t need,
+                         bool static_ws = false) {
   if (d->To > d->Tc) return fail(REHYAT_ERR_UNSUPPORTED, "recurrent step needs To <= Tc");
   const int nch = n_chunks(d);
   if (t < 0 || t >= nch) return fail(REHYAT_ERR_SHAPE, "chunk_index %d outside [0, %d)", t, nch);
@@ -503,9 +505,11 @@ rehyat_status check_step(const rehyat_desc* d, int32_t t, const void* q_c, const
       !aligned16(S) || !aligned16(z) || !aligned16(y_c) ||
       (d->To > 0 && (!aligned16(k_tail) || !aligned16(v_tail))))
     return fail(REHYAT_ERR_ALIGN, "pointers must be 16-byte aligned");
-  if (!ws || ws_bytes < need)
-    return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  if (!aligned16(ws)) return fail(REHYAT_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (!static_ws) {   // (the static scratch array is an allocation of its own)
+    if (!ws || ws_bytes < need)
+      return fail(REHYAT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(REHYAT_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
   const int BH = d->B * d->H;
   const int64_t crow = (int64_t)cf * d->HW;          // rows in this chunk
   const int64_t trow = (int64_t)d->To * d->HW;       // rows in the tail
@@ -659,18 +663,32 @@ size_t rehyat_recurrent_step_fused_workspace(const rehyat_desc* d) {
   return round_up((int64_t)(BH * sizeof(unsigned)), 256) + 3 * BH * state_elems(d) * sizeof(float);
 }
 
-rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* d, int32_t t, const void* q_c,
-                                          const void* k_c, const void* v_c, const void* Wq,
-                                          const void* Wk, float* S, float* z, const void* k_tail,
-                                          const void* v_tail, void* k_tail_out, void* v_tail_out,
-                                          void* y_c, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The single-launch step on the scratch buffer ws (its counters zero on entry, left zero).
+rehyat_status device_scratch(hipStream_t s, void** out);
+
+// static_ws: every argument is checked first, then ws is the current device's static array.
+rehyat_status step_fused_impl(const rehyat_desc* d, int32_t t, const void* q_c, const void* k_c,
+                              const void* v_c, const void* Wq, const void* Wk, float* S, float* z,
+                              const void* k_tail, const void* v_tail, void* k_tail_out,
+                              void* v_tail_out, void* y_c, void* ws, size_t ws_bytes,
+                              void* stream, bool static_ws = false) {
   rehyat_status st = check_desc(d);
   if (st != REHYAT_OK) return st;
   if (d->dtype != REHYAT_BF16 || d->phi_kind != REHYAT_PHI_POLY2)
     return fail(REHYAT_ERR_UNSUPPORTED,
                 "the single-launch step supports bf16 inputs with the fixed feature map");
   const size_t need = rehyat_recurrent_step_fused_workspace(d);
-  st = check_step(d, t, q_c, k_c, v_c, Wq, Wk, S, z, k_tail, v_tail, y_c, ws, ws_bytes, need);
+  if (static_ws && need > (size_t)REHYAT_STATIC_SCRATCH_BYTES)
+    return fail(REHYAT_ERR_WORKSPACE,
+                "the step needs %zu bytes of scratch, beyond the static %d bytes "
+                "(use rehyat_recurrent_step_fused with a workspace)",
+                need, REHYAT_STATIC_SCRATCH_BYTES);
+  st = check_step(d, t, q_c, k_c, v_c, Wq, Wk, S, z, k_tail, v_tail, y_c, ws, ws_bytes, need,
+                  static_ws);
   if (st != REHYAT_OK) return st;
   const int BH = d->B * d->H;
   const int64_t crow = (int64_t)step_frames(d, t) * d->HW;   // rows in this chunk
@@ -694,6 +712,10 @@ rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* d, int32_t t, const
           return fail(REHYAT_ERR_ALIAS, "k_tail_out, v_tail_out must not overlap the other buffers");
     if (overlaps(k_tail_out, nt, v_tail_out, nt))
       return fail(REHYAT_ERR_ALIAS, "k_tail_out and v_tail_out must not overlap");
+  }
+  if (static_ws) {
+    st = device_scratch((hipStream_t)stream, &ws);
+    if (st != REHYAT_OK) return st;
   }
   const size_t E = state_elems(d);
   unsigned* counter = reinterpret_cast<unsigned*>(ws);
@@ -740,6 +762,72 @@ rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* d, int32_t t, const
   const hipError_t e = launch_step_bf16(a, sp, d->F, s);
   timed_end(s, 4);
   return hip_status(e, "step launch");
+}
+
+// ---- scratch without an allocation ------------------------------------------------------
+// The step's scratch (completion counters, the new state, the fold's partials) for
+// rehyat_recurrent_step_fused_noalloc lives in this array: one copy on every device the
+// library runs on, resident until the process ends. Host code never uses the array's name
+// as an address: the device address of each device's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[REHYAT_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_scratch_kernel(u32x4* p, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Device address of the current device's scratch array. The first call on a device looks
+// it up (with that device current) and enqueues a fill kernel on `s` that zeroes the whole
+// array, so that the completion counters start at zero; later calls leave them zero.
+rehyat_status device_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(REHYAT_ERR_UNSUPPORTED, "device %d beyond the %d devices supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(REHYAT_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    const int64_t n16 = REHYAT_STATIC_SCRATCH_BYTES / 16;
+    hipLaunchKernelGGL(zero_scratch_kernel, dim3(256), dim3(256), 0, s,
+                       reinterpret_cast<u32x4*>(p), n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "scratch fill launch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* d, int32_t t, const void* q_c,
+                                          const void* k_c, const void* v_c, const void* Wq,
+                                          const void* Wk, float* S, float* z, const void* k_tail,
+                                          const void* v_tail, void* k_tail_out, void* v_tail_out,
+                                          void* y_c, void* ws, size_t ws_bytes, void* stream) {
+  return step_fused_impl(d, t, q_c, k_c, v_c, Wq, Wk, S, z, k_tail, v_tail, k_tail_out,
+                         v_tail_out, y_c, ws, ws_bytes, stream);
+}
+
+rehyat_status rehyat_recurrent_step_fused_noalloc(const rehyat_desc* d, int32_t t,
+                                                  const void* q_c, const void* k_c,
+                                                  const void* v_c, const void* Wq, const void* Wk,
+                                                  float* S, float* z, const void* k_tail,
+                                                  const void* v_tail, void* k_tail_out,
+                                                  void* v_tail_out, void* y_c, void* stream) {
+  return step_fused_impl(d, t, q_c, k_c, v_c, Wq, Wk, S, z, k_tail, v_tail, k_tail_out,
+                         v_tail_out, y_c, nullptr, REHYAT_STATIC_SCRATCH_BYTES, stream, true);
 }
 
 size_t rehyat_hybrid_bwd_workspace(const rehyat_desc* d) {

@@ -35,7 +35,8 @@
  * Conventions for every entry point
  *   - All tensors are dense, row-major, head-major: [B, H, rows, cols]. Device pointers
  *     must be 16-byte aligned. The caller owns every buffer; the library allocates no
- *     device memory, keeps no state between calls and never synchronises the stream.
+ *     device memory, keeps no state between calls (apart from the static scratch array of
+ *     rehyat_recurrent_step_fused_noalloc) and never synchronises the stream.
  *   - dtype REHYAT_BF16: q, k, v, W (and tails) are bf16; products run on bf16 MFMA with
  *     fp32 accumulation; phi(q), phi(k), the softmax weights and the state are rounded to
  *     bf16 where they enter an MFMA. dtype REHYAT_F32: everything in fp32.
@@ -195,6 +196,35 @@ rehyat_status rehyat_recurrent_step_fused(const rehyat_desc* desc, int32_t chunk
                                           const void* k_tail, const void* v_tail,
                                           void* k_tail_out, void* v_tail_out, void* y_c,
                                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rehyat_recurrent_step_fused for callers that cannot allocate device memory or take a
+ * workspace: code under HIP graph capture, tight serving loops and harnesses that forbid
+ * allocation. The same kernel and results, bit for bit; the scratch (per-head completion
+ * counters, the new state, the fold's partials) comes from a static device array of
+ * REHYAT_STATIC_SCRATCH_BYTES bytes that every device the library runs on holds until the
+ * process ends. The call allocates nothing. Arguments, requirements and results as for
+ * rehyat_recurrent_step_fused, without ws and ws_bytes.
+ *   Limit: rehyat_recurrent_step_fused_workspace(desc) must not exceed
+ *          REHYAT_STATIC_SCRATCH_BYTES (it is 256*ceil(B*H/64) + 12*B*H*(F*D + F) bytes,
+ *          e.g. 2.4 MB for B*H = 12, F = 128); larger descriptors return
+ *          REHYAT_ERR_WORKSPACE before anything is enqueued.
+ *   Device: the array of the calling thread's current device is used; `stream` must belong
+ *          to that device. The first call on a device looks the array up and enqueues a fill
+ *          kernel on `stream` that zeroes it (make that call outside stream capture); every
+ *          call leaves the counters zero again.
+ *   Concurrency: all calls on one device share its array, which keeps the last call's
+ *          contents; calls that overlap in time on one device (other streams, other
+ *          threads) race and must not be issued.
+ */
+#define REHYAT_STATIC_SCRATCH_BYTES (16 * 1024 * 1024)
+rehyat_status rehyat_recurrent_step_fused_noalloc(const rehyat_desc* desc, int32_t chunk_index,
+                                                  const void* q_c, const void* k_c,
+                                                  const void* v_c, const void* Wq,
+                                                  const void* Wk, float* S, float* z,
+                                                  const void* k_tail, const void* v_tail,
+                                                  void* k_tail_out, void* v_tail_out,
+                                                  void* y_c, void* stream);
 
 /*
  * Backward of the non-recursive causal form (key designs 1 and 4: the form the method is

@@ -167,6 +167,44 @@ def test_recurrent_step_fused_validation():
     assert L.rehyat_recurrent_step_fused_workspace(ctypes.byref(_desc(D=64).c())) == 0
 
 
+def step_noalloc(desc, t=1, q=P[0], k=P[1], v=P[2], Wq=P[3], Wk=P[4], S=P[5], z=P[6], kt=P[7],
+                 vt=P[8], y=P[9], ko=P[11], vo=P[12]):
+    L = hs.lib()
+    return L.rehyat_recurrent_step_fused_noalloc(ctypes.byref(desc.c()), t, q, k, v, Wq, Wk, S, z,
+                                                 kt, vt, ko, vo, y, None)
+
+
+def test_recurrent_step_fused_noalloc_validation():
+    """The no-allocation step checks every argument (and its scratch size against the static
+    array) before it looks the array up on a device: every case below returns first."""
+    src = open(HEADER).read()
+    m = re.search(r"#define REHYAT_STATIC_SCRATCH_BYTES \((\d+) \* (\d+) \* (\d+)\)", src)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == hs.STATIC_SCRATCH_BYTES
+    L = hs.lib()
+    d = _desc()
+    assert step_noalloc(_desc(To=4)) == ERR_UNSUP
+    assert step_noalloc(d, t=d.n_chunks) == ERR_SHAPE
+    assert step_noalloc(d, kt=None) == ERR_NULL
+    assert step_noalloc(d, z=P[5] + 4) == ERR_ALIGN
+    assert step_noalloc(d, y=P[2]) == ERR_ALIAS
+    assert step_noalloc(d, ko=P[7]) == ERR_ALIAS
+    assert step_noalloc(_desc(phi_kind=hs.PHI_ELU)) == ERR_UNSUP
+    # the largest B*H whose scratch fits at F = 256 is accepted by the size check, one more
+    # head is refused with REHYAT_ERR_WORKSPACE
+    def need(B, H, F):
+        return L.rehyat_recurrent_step_fused_workspace(ctypes.byref(_desc(B=B, H=H, F=F).c()))
+    H = 1
+    while need(1, H + 1, 256) <= hs.STATIC_SCRATCH_BYTES:
+        H += 1
+    assert need(1, H, 256) <= hs.STATIC_SCRATCH_BYTES < need(1, H + 1, 256)
+    assert step_noalloc(_desc(B=1, H=H + 1, F=256)) == ERR_WS
+    assert "static" in L.rehyat_last_error().decode()
+    assert step_noalloc(_desc(B=1, H=H + 1, F=256), kt=None) == ERR_WS   # size checked first
+    # the 81-frame streaming workload (B1 H12 F128) and B2 H12 at F = 256 fit
+    assert need(1, 12, 128) <= hs.STATIC_SCRATCH_BYTES
+    assert need(2, 12, 256) <= hs.STATIC_SCRATCH_BYTES
+
+
 def test_phi_and_state_update_validation():
     L = hs.lib()
     d = _desc()
