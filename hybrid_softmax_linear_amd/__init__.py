@@ -35,7 +35,9 @@ CAUSAL, BIDIR = 0, 1
 PHI_POLY2, PHI_ELU, PHI_MLP = 0, 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "librehyat.so")
+# REHYAT_LIBRARY names another build of the same library (e.g. the host-sanitized copy that
+# hybrid_softmax_linear_amd.build.build_host_sanitized makes for the host tests)
+library_path = os.environ.get("REHYAT_LIBRARY") or os.path.join(_PKG, "librehyat.so")
 
 
 class RehyatError(RuntimeError):

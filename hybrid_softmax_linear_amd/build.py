@@ -70,5 +70,41 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of ROCm's clang (to preload into a process that
+    loads the sanitized library)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang's shared AddressSanitizer runtime not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_host_sanitized(out: str) -> str:
+    """A copy of librehyat.so whose host code of the C ABI (api.cpp: argument checks,
+    workspace layout, launch sequences) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer; the kernels are the regular objects (device code is not
+    sanitized). For host-side tests only: load it with the runtime from asan_runtime()
+    preloaded. Returns the library path."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o"))
+               for s in SOURCES if s != "api.cpp"):
+        build(verbose=False)
+    obj = os.path.join(BUILD, "api_hostsan.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+    cmd = ([hipcc(), "-x", "hip"] + FLAGS + san + ["-c", os.path.join(CSRC, "api.cpp"), "-o", obj])
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling api.cpp with host sanitizers failed:\n{res.stderr}")
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.cpp"]
+    cmd = ([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-o", out, obj] + objs)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking the sanitized library failed:\n{res.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build()
