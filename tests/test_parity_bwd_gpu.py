@@ -131,11 +131,9 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
-@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16], ids=["y32", "y16"])
-def test_hybrid_bwd_small(case, y_dtype):
-    B, H, T, HW, F, Tc, To, extra = case
-    inp = _inputs(B, H, T, HW, F, seed=hash(case[:7]) % 10000, **extra)
+def _check_all(inp, *, HW, Tc, To, y_dtype, label):
+    """Every entry of dq, dk, dv, dWq and dWk against the oracle (all heads)."""
+    B, H = inp["q"].shape[:2]
     dy, got = _run(inp, HW=HW, Tc=Tc, To=To, y_dtype=y_dtype)
     q, k, v = (to_f64(inp[n]) for n in ("q", "k", "v"))
     dyf = to_f64(dy)
@@ -143,7 +141,6 @@ def test_hybrid_bwd_small(case, y_dtype):
     names = ("dq", "dk", "dv", "dWq", "dWk")
     ref, mag, emu = ({n: np.zeros_like(got[n]) for n in names} for _ in range(3))
     per_head = Wq_t.dim() == 3
-    label = f"bwd {case[:7]} {extra} {'y16' if y_dtype == torch.bfloat16 else 'y32'}"
     for b in range(B):
         for h in range(H):
             Wq, Wk = _w(Wq_t, h), _w(Wk_t, h)
@@ -161,6 +158,26 @@ def test_hybrid_bwd_small(case, y_dtype):
                         dst[n] += src[n]
     for n in names:
         _compare(n, got[n], ref[n], mag[n], emu[n], label)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16], ids=["y32", "y16"])
+def test_hybrid_bwd_small(case, y_dtype):
+    B, H, T, HW, F, Tc, To, extra = case
+    inp = _inputs(B, H, T, HW, F, seed=hash(case[:7]) % 10000, **extra)
+    _check_all(inp, HW=HW, Tc=Tc, To=To, y_dtype=y_dtype,
+               label=f"bwd {case[:7]} {extra} {'y16' if y_dtype == torch.bfloat16 else 'y32'}")
+
+
+@pytest.mark.parametrize("extra", [{}, {"w_gain": 12.0, "w_per_head": True, "separate_wk": True}],
+                         ids=["workload_map", "strong_per_head_maps"])
+def test_hybrid_bwd_mid_size_every_entry(extra):
+    """A mid-size shape (B1 H3, 9 frames of 520 tokens: 3 chunks of 1560 queries, Tc3 To1,
+    F128) with every entry of dq, dk, dv and of the feature-map gradients dWq, dWk checked:
+    the full-size test samples rows of one head and cannot check dW, which sums over all
+    rows and heads."""
+    inp = _inputs(1, 3, 9, 520, 128, seed=77, **extra)
+    _check_all(inp, HW=520, Tc=3, To=1, y_dtype=torch.float32, label=f"bwd mid-size {extra}")
 
 
 

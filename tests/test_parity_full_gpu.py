@@ -49,6 +49,47 @@ def test_full_workload_whole_sequence(i):
     _check_rows(y_rows, ref, inp, cfg, rows, cfg.name)
 
 
+def test_c2_bidirectional_every_row():
+    """The 320x480 bidirectional workload (B1 H12, 21x20x30, Tc3 To1) on every query row of
+    every head: its complement linear sets and all eight query tiles per chunk (the last one
+    ragged), with no recurrent form to cross-check it bitwise."""
+    cfg = syn.config(2)
+    inp = syn.make_inputs(cfg)
+    _, y = _fwd(cfg, inp)
+    y = y.double().cpu().numpy()
+    assert np.isfinite(y).all()
+    ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=False)
+    _check_rows(y, ref, inp, cfg, list(range(cfg.N)), cfg.name + " every row")
+
+
+@pytest.mark.parametrize("i", [2, 3, 5])
+def test_fp32_path_at_workload_shape(i):
+    """The fp32 path (fp32 q, k, v, W, y) at the shapes of the 320x480, 21x30x52 and
+    wide-chunk workloads, on sampled rows of every head against the oracle at the fp32 bar
+    (1e-4): a check of the sets and the normalisation free of bf16 rounding. The inputs
+    follow the fp32 workload's recipe (q, k, v ~ N(0, 1), W ~ N(0, 1/D)): with the
+    21x30x52 workload's per-head scale (logits of standard deviation up to 4) the fp32
+    rounding of the logits alone reaches that bar (1.0e-4 measured at |y| up to 6)."""
+    cfg = syn.config(i)
+    inp = syn.make_custom(cfg.B, cfg.H, cfg.N, cfg.D, cfg.F, seed=cfg.seed + 100, dtype="f32",
+                          HW=cfg.HW)
+    d = {k: v.to(DEV) for k, v in inp.items() if k in ("q", "k", "v", "W")}
+    y = ta.hybrid_fwd(d["q"], d["k"], d["v"], d["W"], HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
+                      causal=cfg.mode == "causal", y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = pu.sample_rows(cfg.T, cfg.HW, cfg.Tc, per_edge=8, n_random=24, seed=i + 10)
+    y_rows = y[:, :, rows].double().cpu().numpy()
+    del d, y
+    ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=cfg.mode == "causal",
+                         rows=rows)
+    errs = pu.chunk_errors(y_rows, ref, rows, cfg.T, cfg.HW, cfg.Tc)
+    err = max(e["max_abs"] for e in errs)
+    print(f"[fp32 path, {cfg.name} shape] max-abs {err:.3e} (bar {pu.F32_BAR:.0e}); "
+          f"{pu.describe(errs)}", flush=True)
+    assert np.isfinite(y_rows).all()
+    assert err <= pu.F32_BAR
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["multi_launch", "single_launch"])
 @pytest.mark.parametrize("i", [3, 5])
 def test_full_workload_recurrent_equals_whole(i, fused):

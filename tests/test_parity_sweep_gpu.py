@@ -1,12 +1,15 @@
 """GPU parity over the chunk-size / overlap grid of the pages' ablation (Tc in {1, 2, 3, 5,
 7}, To in {0, 1, 2, 3}; papernotes.org ReHyAt note, key hyper-parameters and ablation
-sections) at the 21x20x30 latent (320x480), causal form, bf16 inputs, fp32 output, in the
-launch configuration bench.py --sweep times. To > Tc (a window reaching further back
-than one chunk) is part of the grid.
+sections) at the 21x20x30 latent (320x480, B1 H12) and the 21x30x52 latent (480x832, B2
+H12 with per-head scales), causal form, bf16 inputs, fp32 output, in the launch
+configuration bench.py --sweep times. To > Tc (a window reaching further back than one
+chunk) is part of the grid.
 
 Sampled query rows (first and last rows of every chunk plus random rows) of three heads
-are checked against the float64 oracle with the same bars as the other bf16 tests.
+per grid point are checked against the float64 oracle with the same bars as the other
+bf16 tests.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -19,27 +22,38 @@ DEV = "cuda"
 GRID = [(tc, to) for tc in (1, 2, 3, 5, 7) for to in (0, 1, 2, 3)]
 
 
-@pytest.fixture(scope="module")
-def inputs():
-    cfg = syn.config(2)   # 21x20x30, B1 H12 D128 F128
+# the two latents; heads checked per grid point
+LATENTS = {"21x20x30": (2, [(0, 0), (0, 5), (0, 11)]),
+           "21x30x52": (3, [(0, 0), (1, 6), (1, 11)])}
+
+
+@pytest.fixture(scope="module", params=sorted(LATENTS))
+def inputs(request):
+    i, heads = LATENTS[request.param]
+    cfg = syn.config(i)
     inp = syn.make_inputs(cfg)
     dev = {k: v.to(DEV) for k, v in inp.items() if k in ("q", "k", "v", "W")}
-    return cfg, inp, dev
+    yield cfg, inp, dev, heads
+    del dev
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("Tc,To", GRID, ids=[f"Tc{a}_To{b}" for a, b in GRID])
 def test_sweep_grid_sampled_rows(inputs, Tc, To):
-    cfg, inp, d = inputs
+    cfg, inp, d, heads = inputs
     y = ta.hybrid_fwd(d["q"], d["k"], d["v"], d["W"], HW=cfg.HW, Tc=Tc, To=To, causal=True,
                       y_dtype=torch.float32)
     torch.cuda.synchronize()
     rows = pu.sample_rows(cfg.T, cfg.HW, Tc, per_edge=4, n_random=16, seed=Tc * 10 + To)
-    heads = [(0, 0), (0, 5), (0, 11)]
     y_rows = y[:, :, rows].double().cpu().numpy()
     ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=Tc, To=To, causal=True, rows=rows, heads=heads)
-    sel = [h for (_, h) in heads]
-    errs = pu.chunk_errors(y_rows[:, sel], ref[:, sel], rows, cfg.T, cfg.HW, Tc)
+    bi = [b for (b, _) in heads]
+    hi = [h for (_, h) in heads]
+    got, want = y_rows[bi, hi][None], ref[bi, hi][None]
+    errs = pu.chunk_errors(got, want, rows, cfg.T, cfg.HW, Tc)
     err = max(e["max_abs"] for e in errs)
     rel = max(pu.chunk_rel_errors(errs))
-    print(f"[Tc={Tc} To={To}] max-abs {err:.3e}, max per-chunk relative {rel:.2e}", flush=True)
+    print(f"[{cfg.name} Tc={Tc} To={To}] max-abs {err:.3e}, max per-chunk relative {rel:.2e}",
+          flush=True)
+    assert np.isfinite(got).all()
     pu.assert_bf16(errs, False)
