@@ -19,6 +19,8 @@ whole sequence) with librehyat and with torch's SDPA.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-context]
     python bench.py --phi mlp|elu   the same line with another feature map of key design 3
+    python bench.py --workload c2|c5   the same line for the 21x20x30 bidirectional (320x480)
+                                or the 49x30x52 wide-chunk (Tc 7, To 3, F 256) workload
     python bench.py --sweep     (Tc, To) grid of the ablation, one JSON line per entry
     python bench.py --bwd       the backward of the causal form on the same workload
     python bench.py --stream    the 81x30x52 streaming workload: 27 single-launch recurrent
@@ -424,6 +426,10 @@ def main(argv=None):
     ap.add_argument("--bwd", action="store_true",
                     help="instead of the default line: the backward of the causal form "
                          "(rehyat_hybrid_bwd) on the same workload")
+    ap.add_argument("--workload", choices=("c3", "c2", "c5"), default="c3",
+                    help="whole-sequence workload of the line: c3 the 21x30x52 causal latent "
+                         "(the metric's, default), c2 the 21x20x30 bidirectional latent "
+                         "(320x480, B1), c5 the 49x30x52 wide-chunk latent (Tc 7, To 3, F 256)")
     ap.add_argument("--phi", choices=("poly2", "elu", "mlp"), default="poly2",
                     help="feature map of the timed step (default: the fixed map)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -447,9 +453,11 @@ def main(argv=None):
         return bench_bwd(args)
     if args.stream:
         return bench_stream(args)
-    cfg = syn.config(3)
+    cfg = syn.config(int(args.workload[1]))
+    headline = args.workload == "c3"
+    causal = cfg.mode == "causal"
     inp = syn.make_inputs(cfg)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
+    cpu = None if (args.no_cpu_baseline or not headline) else cpu_baseline(inp, cfg)
     print(f"# cpu baseline done: {cpu and round(cpu['value'], 1)} tokens/s", file=sys.stderr,
           flush=True)
 
@@ -463,7 +471,7 @@ def main(argv=None):
         del src, dst
     q, k, v, W = (inp[n].to(dev) for n in ("q", "k", "v", "W"))
     base = dict(B=cfg.B, H=cfg.H, T=cfg.T, HW=cfg.HW, D=cfg.D, Tc=cfg.Tc, To=cfg.To,
-                dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL)
+                dtype=hs.BF16, y_dtype=hs.F32, mode=hs.CAUSAL if causal else hs.BIDIR)
     fields, Wq, Wk, phi_flop, phi_label = feature_map_setup(args.phi, cfg, dev)
     Wq = W if Wq is None and args.phi == "poly2" else Wq
     Wk = W if Wk is None and args.phi == "poly2" else Wk
@@ -487,7 +495,7 @@ def main(argv=None):
     dist = step_distribution(step, 50)
 
     total_flop, attn_flop, state_flop, pairs = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D,
-                                                          desc.F, cfg.Tc, cfg.To, causal=True,
+                                                          desc.F, cfg.Tc, cfg.To, causal=causal,
                                                           phi_row_flop=phi_flop)
     tokens = cfg.B * cfg.N
     tflops = total_flop / (ms * 1e-3) / 1e12
@@ -496,7 +504,7 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     context = {}
-    if not args.no_context and args.phi == "poly2":
+    if not args.no_context and args.phi == "poly2" and headline:
         # the other feature maps of key design 3, same workload
         for kind in ("mlp", "elu"):
             f2, wq2, wk2, pf2, _ = feature_map_setup(kind, cfg, dev)
@@ -512,7 +520,7 @@ def main(argv=None):
             context[f"{name}_tokens_per_s"] = tokens / (ms2 * 1e-3)
             context[f"{name}_tflops"] = fl2 / (ms2 * 1e-3) / 1e12
             del ws2, wq2, wk2
-    if not args.no_context and args.phi == "poly2":
+    if not args.no_context and args.phi == "poly2" and headline:
         # the same causal computation as 7 recurrent steps (chunks resident, contiguous)
         Np = cfg.Tc * cfg.HW
         chunks = [tuple(x[:, :, t * Np:(t + 1) * Np].contiguous() for x in (q, k, v))
@@ -558,8 +566,20 @@ def main(argv=None):
         except Exception as e:  # third-party context only
             context["torch_sdpa_error"] = str(e)[:200]
 
+    if headline:
+        metric = METRIC
+        workload = (f"21x30x52 latent (480x832, 5 s): B2 H12 D128 F{desc.F}, Tc3 To1, causal, "
+                    f"one rehyat_hybrid_fwd call per step"
+                    + ("" if args.phi == "poly2" else f", {phi_label}"))
+    else:
+        lat = f"{cfg.T}x{cfg.HW // (52 if cfg.HW == 1560 else 30)}x{52 if cfg.HW == 1560 else 30}"
+        form = "causal" if causal else "bidirectional"
+        metric = f"hybrid-attn tokens/s & TFLOP/s per MI355X at {lat.replace('x', '×')} ({form}), % of MFMA peak"
+        workload = (f"{lat} latent: B{cfg.B} H{cfg.H} D{cfg.D} F{desc.F}, Tc{cfg.Tc} To{cfg.To}, "
+                    f"{form}, one rehyat_hybrid_fwd call per step"
+                    + ("" if args.phi == "poly2" else f", {phi_label}"))
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": tokens / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -571,18 +591,17 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"21x30x52 latent (480x832, 5 s): B2 H12 D128 F{desc.F}, Tc3 "
-                               f"To1, causal, one rehyat_hybrid_fwd call per step"
-                               + ("" if args.phi == "poly2" else f", {phi_label}"),
+        "config": {"workload": workload,
                    "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)",
                    "y_dtype": "fp32"},
         "tflops": tflops,
         "mfma_peak_frac": tflops / MFMA_PEAK_BF16_TFLOPS,
         "flop_per_step": total_flop,
         "step_ms_distribution": dist,
-        "roofline": {"bound": "mfma", "kernel": "hybrid_attn_bf16_kernel<128>",
+        "roofline": {"bound": "mfma", "kernel": f"hybrid_attn_bf16_kernel<{desc.F}>",
                      "achieved": attn_tflops, "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic() if headline and args.phi == "poly2" else None,
                      "flop_per_launch": attn_flop, "avg_launch_ms": kern_avg,
                      "launches_timed": launches},
         "cpu_baseline": cpu,

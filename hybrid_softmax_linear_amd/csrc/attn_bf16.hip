@@ -72,14 +72,40 @@ struct Geo {
 // is in two segments (the carried tail, then the chunk): window rows [0, na) come from
 // k / v, the rest from k2 / v2, whose base sits na rows before the chunk's first row so
 // that one byte offset (window row * 256 + column) addresses either segment.
+typedef int i32x4 __attribute__((ext_vector_type(4)));   // buffer descriptor words
+
 struct Src {
-  __amdgpu_buffer_rsrc_t k;     // base = first window row, range = nk rows (na rows: step)
-  __amdgpu_buffer_rsrc_t v;
-  __amdgpu_buffer_rsrc_t k2;    // step: base = chunk row 0 - na rows, range = nk rows
-  __amdgpu_buffer_rsrc_t v2;
+  i32x4 k;                      // base = first window row, range = nk rows (na rows: step)
+  i32x4 v;
+  i32x4 k2;                     // step: base = chunk row 0 - na rows, range = nk rows
+  i32x4 v2;
   int nk;                       // window length
   int na_bytes;                 // step: 256 x the window rows in the first segment
 };
+
+// Buffer descriptor words of [base, base + bytes) (raw buffer, stride 0).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xffffu), bytes, kBufRsrcWord3};
+}
+
+// One direct-to-LDS buffer load (16 bytes per lane into lds + 16 lane; bytes past the
+// descriptor's range read as zero), written in asm so that the compiler does not track it:
+// the compiler makes the first transposing LDS read after a direct-to-LDS load it knows of
+// wait for every such load in flight, which would wait for the next tile's loads one block
+// after they are issued. The kernel orders these loads itself (a vmcnt(0) wait before the
+// barrier that hands a stage over). The load has no register result; M0 carries the LDS
+// address.
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
+  return (unsigned)(uintptr_t)(lds_void*)p;
+}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }   // vmcnt(0) lgkmcnt(0)
@@ -95,12 +121,12 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // (pad slots 16 and 17 copy chunk 0). 34 + 36 instructions per tile, spread over the 8
 // waves. kSplit: a lane whose byte offset lies past na_bytes loads from (k2, v2) instead
 // (the two loads of an instruction that straddles the boundary write disjoint lanes' slots).
-template <bool kSplit>
-__device__ __forceinline__ void tile_dma_from(__amdgpu_buffer_rsrc_t k, __amdgpu_buffer_rsrc_t v,
-                                              const Src& s, int kt, unsigned char* stage,
-                                              int wave, int lane) {
+template <bool kSplit, int kPart = 2>
+__device__ __forceinline__ void tile_dma_from(i32x4 k, i32x4 v, const Src& s, int kt,
+                                              unsigned char* stage, int wave, int lane) {
+  const unsigned sl = lds_addr(stage);
 #pragma unroll
-  for (int i = 0; i < (kDmaInsts + NW - 1) / NW; ++i) {
+  for (int i = 0; i < (kPart == 1 ? 0 : (kDmaInsts + NW - 1) / NW); ++i) {
     const int j = wave + NW * i;
     if (j < kDmaInsts) {
       const int u = 64 * j + lane;
@@ -109,14 +135,13 @@ __device__ __forceinline__ void tile_dma_from(__amdgpu_buffer_rsrc_t k, __amdgpu
       c = c == 16 ? 0 : c;
       const int off = (kt * kKeys + r) * 256 + c * 16;
       if (!kSplit || off < s.na_bytes)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(k, (lds_void*)(stage + j * 1024), 16, off, 0, 0, 0);
+        dma16(k, sl + j * 1024, off);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k2, (lds_void*)(stage + j * 1024), 16, off, 0,
-                                                 0, 0);
+        dma16(s.k2, sl + j * 1024, off);
     }
   }
 #pragma unroll
-  for (int i = 0; i < (kVInsts + NW - 1) / NW; ++i) {
+  for (int i = 0; i < (kPart == 0 ? 0 : (kVInsts + NW - 1) / NW); ++i) {
     const int j = wave + NW * i;
     if (j < kVInsts) {
       const int u = 64 * j + lane;
@@ -125,11 +150,9 @@ __device__ __forceinline__ void tile_dma_from(__amdgpu_buffer_rsrc_t k, __amdgpu
       c = c >= 16 ? 0 : c;
       const int off = (kt * kKeys + r) * 256 + c * 16;
       if (!kSplit || off < s.na_bytes)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(v, (lds_void*)(stage + kKBytes + j * 1024), 16,
-                                                 off, 0, 0, 0);
+        dma16(v, sl + kKBytes + j * 1024, off);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.v2, (lds_void*)(stage + kKBytes + j * 1024),
-                                                 16, off, 0, 0, 0);
+        dma16(s.v2, sl + kKBytes + j * 1024, off);
     }
   }
 }
@@ -137,20 +160,21 @@ __device__ __forceinline__ void tile_dma_from(__amdgpu_buffer_rsrc_t k, __amdgpu
 // kTwo: the window is in two segments. A tile wholly inside one of them takes that
 // segment's descriptors (a uniform choice); only the tile that straddles the boundary
 // chooses per lane.
-template <bool kTwo>
+// kPart: 0 the K loads, 1 the V loads, 2 both.
+template <bool kTwo, int kPart = 2>
 __device__ __forceinline__ void tile_dma(const Src& s, int kt, unsigned char* stage, int wave,
                                          int lane) {
   if (!kTwo) {
-    tile_dma_from<false>(s.k, s.v, s, kt, stage, wave, lane);
+    tile_dma_from<false, kPart>(s.k, s.v, s, kt, stage, wave, lane);
     return;
   }
   const int t0 = kt * kKeys * 256;
   if (t0 < s.na_bytes && t0 + kKeys * 256 > s.na_bytes) {
-    tile_dma_from<true>(s.k, s.v, s, kt, stage, wave, lane);
+    tile_dma_from<true, kPart>(s.k, s.v, s, kt, stage, wave, lane);
   } else if (t0 < s.na_bytes) {
-    tile_dma_from<false>(s.k, s.v, s, kt, stage, wave, lane);
+    tile_dma_from<false, kPart>(s.k, s.v, s, kt, stage, wave, lane);
   } else {
-    tile_dma_from<false>(s.k2, s.v2, s, kt, stage, wave, lane);
+    tile_dma_from<false, kPart>(s.k2, s.v2, s, kt, stage, wave, lane);
   }
 }
 
@@ -444,11 +468,12 @@ __device__ __forceinline__ void scale_linear(Acc& A, float nl, float m0, int lan
 // tile has landed, the barrier passes and the next tile's block-0 fragments are requested
 // before block 3's exponentials (kf and vf hold them on exit), so the pipeline does not
 // drain at tile boundaries.
-template <bool kLastTile>
+template <bool kLastTile, bool kTwo>
 __device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned char* stage,
-                                             const unsigned char* next_stage, int kt, int nk,
-                                             const QRegs& Q, float ls, int lane,
-                                             bf16x8 (&kf)[8], bf16x8 (&vf)[4][2]) {
+                                             unsigned char* next_stage, int kt, int nk,
+                                             const QRegs& Q, float ls, int wave, int lane,
+                                             const Src& src, bf16x8 (&kf)[8],
+                                             bf16x8 (&vf)[4][2]) {
   const unsigned char* kbuf = stage;
   const unsigned char* vbuf = stage + kKBytes;
 #pragma unroll
@@ -456,6 +481,10 @@ __device__ __forceinline__ void process_tile(Acc& A, float m0, const unsigned ch
     const int key0 = kt * kKeys + kb * 32;
     if (kLastTile && key0 >= nk) break;
     f32x16 S = qk_mfma(kf, Q);
+    // the next tile's loads, in two parts under the first two blocks' MFMAs (the stage they
+    // fill was released at the last tile's barrier)
+    if (!kLastTile && kb == 0) tile_dma<kTwo, 0>(src, kt + 1, next_stage, wave, lane);
+    if (!kLastTile && kb == 1) tile_dma<kTwo, 1>(src, kt + 1, next_stage, wave, lane);
     bf16x8 vn[4][2];
     if (kb < 3) {
       load_k(kf, kbuf, kb + 1, lane);
@@ -523,17 +552,18 @@ __device__ __forceinline__ void key_loop(Acc& A, float m0, const Src& src, const
   for (int kt = 0; kt < ntiles - 1; ++kt) {
     unsigned char* cur = smem + (kt & 1) * kStageBytes;
     unsigned char* nxt = smem + ((kt & 1) ^ 1) * kStageBytes;
-    tile_dma<kTwo>(src, kt + 1, nxt, wave, lane);
     if (active) {
-      process_tile<false>(A, m0, cur, nxt, kt, nk, Q, ls, lane, kf, vf);
+      process_tile<false, kTwo>(A, m0, cur, nxt, kt, nk, Q, ls, wave, lane, src, kf, vf);
     } else {
+      tile_dma<kTwo>(src, kt + 1, nxt, wave, lane);
       wait_vmem_lds();
       __syncthreads();
     }
   }
   const int kt = ntiles - 1;
   if (active)
-    process_tile<true>(A, m0, smem + (kt & 1) * kStageBytes, smem, kt, nk, Q, ls, lane, kf, vf);
+    process_tile<true, kTwo>(A, m0, smem + (kt & 1) * kStageBytes, smem, kt, nk, Q, ls, wave, lane,
+                             src, kf, vf);
   __syncthreads();
 }
 
@@ -652,22 +682,18 @@ __device__ __forceinline__ int attention_block(const AttnArgs& a, int b, unsigne
       src.na_bytes = na * 256;
       const int64_t ah = head_off(g.bh, a.a_rows, kDim) + (a.a_rows - na) * kDim;
       const int64_t bh0 = head_off(g.bh, a.b_rows, kDim) - (int64_t)na * kDim;
-      src.k = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(reinterpret_cast<const uint16_t*>(a.ka) + ah), (short)0, na * 256, kBufRsrcWord3);
-      src.v = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(reinterpret_cast<const uint16_t*>(a.va) + ah), (short)0, na * 256, kBufRsrcWord3);
-      src.k2 = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(reinterpret_cast<const uint16_t*>(a.kb) + bh0), (short)0, nk * 256, kBufRsrcWord3);
-      src.v2 = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(reinterpret_cast<const uint16_t*>(a.vb) + bh0), (short)0, nk * 256, kBufRsrcWord3);
+      src.k = rsrc_words(reinterpret_cast<const uint16_t*>(a.ka) + ah, na * 256);
+      src.v = rsrc_words(reinterpret_cast<const uint16_t*>(a.va) + ah, na * 256);
+      src.k2 = rsrc_words(reinterpret_cast<const uint16_t*>(a.kb) + bh0, nk * 256);
+      src.v2 = rsrc_words(reinterpret_cast<const uint16_t*>(a.vb) + bh0, nk * 256);
     } else {
       src.na_bytes = nk * 256;
       const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.ka) +
                               head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
-      src.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nk * 256, kBufRsrcWord3);
+      src.k = rsrc_words(kbase, nk * 256);
       const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.va) +
                               head_off(g.bh, a.a_rows, kDim) + (a.step ? 0 : g.lo) * kDim;
-      src.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nk * 256, kBufRsrcWord3);
+      src.v = rsrc_words(vbase, nk * 256);
       src.k2 = src.k;
       src.v2 = src.v;
     }
