@@ -48,7 +48,6 @@ constexpr int kVRow = 288;                               // V row: 256 B + 32 B 
 constexpr int kVInsts = kKeys * (kVRow / 16) / 64;       // 36
 constexpr int kVBytes = kKeys * kVRow;                   // V tile [128 keys][128 d] bf16
 constexpr int kStageBytes = kKBytes + kVBytes;           // 70 KB per stage
-constexpr int kBufRsrcWord3 = 0x00020000;                // gfx9 buffer descriptor word 3
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -72,8 +71,6 @@ struct Geo {
 // is in two segments (the carried tail, then the chunk): window rows [0, na) come from
 // k / v, the rest from k2 / v2, whose base sits na rows before the chunk's first row so
 // that one byte offset (window row * 256 + column) addresses either segment.
-typedef int i32x4 __attribute__((ext_vector_type(4)));   // buffer descriptor words
-
 struct Src {
   i32x4 k;                      // base = first window row, range = nk rows (na rows: step)
   i32x4 v;
@@ -82,30 +79,6 @@ struct Src {
   int nk;                       // window length
   int na_bytes;                 // step: 256 x the window rows in the first segment
 };
-
-// Buffer descriptor words of [base, base + bytes) (raw buffer, stride 0).
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, int bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  return i32x4{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xffffu), bytes, kBufRsrcWord3};
-}
-
-// One direct-to-LDS buffer load (16 bytes per lane into lds + 16 lane; bytes past the
-// descriptor's range read as zero), written in asm so that the compiler does not track it:
-// the compiler makes the first transposing LDS read after a direct-to-LDS load it knows of
-// wait for every such load in flight, which would wait for the next tile's loads one block
-// after they are issued. The kernel orders these loads itself (a vmcnt(0) wait before the
-// barrier that hands a stage over). The load has no register result; M0 carries the LDS
-// address.
-__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
-  return (unsigned)(uintptr_t)(lds_void*)p;
-}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }   // vmcnt(0) lgkmcnt(0)

@@ -2,14 +2,16 @@
 //   dS = phi(K_seg)^T V_seg (F x D, fp32) and dz = sum phi(K_seg), phi(x) = 1 + u + u^2/2,
 //   u = x W / sqrt(D)
 // (the sums s_t, z_t of the chunk-wise RNN, papernotes.org ReHyAt note, key design 4).
-// The body is shared by the state kernel (one segment per 256-thread workgroup) and the
-// single-launch recurrent step (two segments per 512-thread workgroup), so both produce
-// the same bits.
+// The state kernel (one segment per workgroup of 4 waves) streams 32-row tiles of K and V
+// into LDS stages by direct-to-LDS loads (partial_issue) and reduces every tile with
+// partial_tile; the fold workgroup of the single-launch recurrent step (two segments per
+// 512-thread workgroup) stages 64-row tiles through registers (segment_sums). Both take the
+// same operand values in the same MFMA chain order, so they produce the same bits.
 //
-// U = K W is computed with K rows as the A operand (rows loaded in kappa order) and W^T
-// as the B operand; its C tile has lane = feature and element i = key cidx(i, lane), which
-// is exactly the A operand phi(K)^T of dS = phi(K)^T V. V enters as the B operand from
-// the transposed V^T tile.
+// U = K W is computed with K rows as the A operand (rows read in kappa order) and W^T as
+// the B operand, held in registers; its C tile has lane = feature and element i = key
+// cidx(i, lane), which is exactly the A operand phi(K)^T of dS = phi(K)^T V. V enters as
+// the B operand through transposing reads of the row-major V tile.
 #pragma once
 
 #include "tiles_bf16.h"
@@ -23,15 +25,19 @@ struct FBlocks {
   static constexpr int per_wave = total >= 4 ? total / 4 : 1;
 };
 
-// LDS of one segment's tiles (K tile + V^T tile); W^T takes F * 256 more.
-constexpr int kPartialTileBytes = kKTileBytes + kVTileBytes;
-
 // Rows of segment seg: [seg * seg_len, min(+seg_len, n)).
 __device__ __forceinline__ int segment_rows(const StateArgs& a, int seg) {
   const int64_t r0 = (int64_t)seg * a.seg_len;
   const int64_t r1 = (r0 + a.seg_len < a.n) ? r0 + a.seg_len : a.n;
   return (int)(r1 - r0);
 }
+
+// ---- register-staged 64-row tiles (the fold workgroup of the single-launch step) ----
+// The same values and MFMA chains as partial_tile over the segment's 32-row tiles, so the
+// fold and the state kernel produce the same bits.
+// LDS of one segment's tiles (K tile + V^T tile); W^T takes F * 256 more.
+constexpr int kPartialTileBytes = kKTileBytes + kVTileBytes;
+
 __device__ __forceinline__ int segment_tiles(const StateArgs& a, int seg) {
   return (segment_rows(a, seg) + kTileRows - 1) / kTileRows;
 }
@@ -180,16 +186,109 @@ __device__ __forceinline__ void for_partial(const PartialRegs<F, kPart>& R, int 
   }
 }
 
-// Partial sums of segment seg of head bh into a.part[bh][seg] (segment_sums, then stores).
-template <int F>
-__device__ __forceinline__ void segment_partial(const StateArgs& a, int bh, int seg, int ntiles,
-                                                const unsigned char* wt, unsigned char* kt,
-                                                unsigned char* vt, int tid) {
-  PartialRegs<F> R;
-  segment_sums<F>(R, a, bh, seg, ntiles, wt, kt, vt, tid);
-  if (!partial_active<F>(seg, tid)) return;
-  float* out = a.part + ((int64_t)bh * a.n_seg + seg) * (F * kDim + F);
-  for_partial<F>(R, tid, [&](int e, float v) { out[e] = v; });
+// ---- direct-to-LDS 32-row tiles (the state kernel) --------------------------------
+// Tiles of 32 rows in LDS. K slot u of the 9 KB K region holds row u / 17, chunk u % 17
+// (rows of 272 B: the 16-byte pad slot takes a copy of chunk 0; the slots past 32 rows hold
+// rows of the next tile, unused); V slot u of the V region holds row u / 18, chunk u % 18
+// (rows of 288 B, pad slots 16 and 17 copy chunk 0). Rows past the segment come back as
+// zeros from the descriptor's range.
+constexpr int kPRows = 32;                    // rows per tile
+constexpr int kPKRow = 272;                   // K row: 256 B + 16 B pad
+constexpr int kPVRow = 288;                   // V row: 256 B + 32 B pad
+constexpr int kPInsts = 9;                    // 1 KB DMA instructions per tile and tensor
+constexpr int kPRegion = kPInsts * 1024;      // 9 KB each for K and V
+constexpr int kPStage = 2 * kPRegion;         // 18 KB
+
+// This wave's direct-to-LDS loads of tile t (rows 32 t ..) of the segment whose K and V
+// rows the descriptors kr, vr cover, into the stage at LDS address st: instructions
+// j = wave + kWaves i of the tile's 2 * kPInsts.
+template <int kWaves>
+__device__ __forceinline__ void partial_issue(i32x4 kr, i32x4 vr, unsigned st, int t, int wave,
+                                              int lane) {
+#pragma unroll
+  for (int i = 0; i < (2 * kPInsts + kWaves - 1) / kWaves; ++i) {
+    const int j = wave + kWaves * i;
+    if (j < kPInsts) {
+      const int u = 64 * j + lane;
+      const int r = u / 17;
+      int c = u - 17 * r;
+      c = c == 16 ? 0 : c;
+      dma16(kr, st + j * 1024, (t * kPRows + r) * 256 + c * 16);
+    } else if (j < 2 * kPInsts) {
+      const int jj = j - kPInsts;
+      const int u = 64 * jj + lane;
+      const int r = u / 18;
+      int c = u - 18 * r;
+      c = c >= 16 ? 0 : c;
+      dma16(vr, st + kPRegion + jj * 1024, (t * kPRows + r) * 256 + c * 16);
+    }
+  }
+}
+
+// Loads one wave issues per tile in partial_issue<kWaves>.
+template <int kWaves>
+__device__ __forceinline__ int partial_insts(int wave) {
+  return (2 * kPInsts - wave + kWaves - 1) / kWaves;
+}
+
+// One 32-row tile (rows key0 .. key0 + 31 of a segment of nrows rows) for feature block fb
+// of this wave and the NDB value blocks db0 .. db0 + NDB - 1: U = K W (wf: W^T rows
+// 32 fb + l % 32 as B operand fragments), p = phi(U) rounded to bf16 (zero past nrows),
+// zp += sum of this lane's p, acc[i] += P^T V[:, 32 (db0 + i) ..]. Element i of acc[b] of
+// lane l is dS[32 fb + crow(i, l)][32 (db0 + b) + l mod 32]; the pair sum of zp over all
+// tiles is dz[32 fb + l mod 32].
+template <int NDB>
+__device__ __forceinline__ void partial_tile(const unsigned char* kt, const unsigned char* vt,
+                                             const bf16x8 (&wf)[8], int key0, int nrows,
+                                             float u_scale, int db0, int lane,
+                                             f32x16 (&acc)[NDB], float& zp) {
+  f32x16 U;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) U[i] = 0.0f;
+  const int arow = kappa(lane & 31);
+  bf16x8 kf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    kf[s] = as_bf16x8(lds_read16(kt, arow * kPKRow + (2 * s + (lane >> 5)) * 16));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) U = mfma32(kf[s], wf[s], U);
+  bf16x8 Pk[2];
+  float zsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i0 = 8 * j + 2 * e;
+      const int key = key0 + cidx(i0, lane);
+      float u0 = U[i0] * u_scale, u1 = U[i0 + 1] * u_scale;
+      float p0 = (key < nrows) ? 1.0f + u0 + 0.5f * u0 * u0 : 0.0f;
+      float p1 = (key + 1 < nrows) ? 1.0f + u1 + 0.5f * u1 * u1 : 0.0f;
+      unsigned w = pack_bf16_u32(p0, p1);
+      zsum += bf16_lo(w) + bf16_hi(w);
+      pk[e] = w;
+    }
+    Pk[j] = as_bf16x8(pk);
+  }
+  zp += zsum;
+  bf16x8 vf[NDB][2];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vf[b][j] = frag_tr(vt, kPVRow, 16 * j, 32 * (db0 + b), lane);
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[b] = mfma32(Pk[j], vf[b][j], acc[b]);
+}
+
+// W^T rows 32 fb + l % 32 (staged in the K-tile layout at wt) as the B operand fragments
+// of U = K W.
+__device__ __forceinline__ void partial_wt_frags(bf16x8 (&wf)[8], const unsigned char* wt,
+                                                 int fb, int lane) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    wf[s] = as_bf16x8(lds_read16(wt, ktile_off(32 * fb + (lane & 31), 2 * s + (lane >> 5))));
 }
 
 }  // namespace rehyat

@@ -1,7 +1,7 @@
 // state_bf16.hip - linear-branch state on bf16 MFMA (gfx950), D = 128:
 //   * per-segment partial sums  dS = phi(K_seg)^T V_seg  (F x D, fp32) and dz = sum phi(K_seg)
 //     (the sums s_t, z_t of the chunk-wise RNN, papernotes.org ReHyAt note, key design 4),
-//     one segment per workgroup (the body is in partial_bf16.h);
+//     one segment per workgroup (the tile loads and reductions are in partial_bf16.h);
 //   * the feature map phi(x) = 1 + u + u^2/2, u = x W / sqrt(D), as a standalone op.
 #include "partial_bf16.h"
 
@@ -10,35 +10,12 @@ namespace rehyat {
 namespace {
 
 // Per-segment partials, one segment per workgroup of 4 waves, two workgroups per CU. The
-// kernel is bound by HBM latency, so tiles of 32 rows stream into four LDS stages by
-// direct-to-LDS loads (up to three in flight while one is reduced; each tile's loads are
-// issued after the previous tile's transposing reads, which wait for all loads in flight)
-// and the W^T operand stays in registers. The operand values and the order of every MFMA chain are those of
-// segment_partial (partial_bf16.h): the results are the same bits.
-constexpr int kBufWord3 = 0x00020000;         // gfx9 buffer descriptor word 3 (raw, 32-bit data)
-constexpr int kPRows = 32;                    // rows per tile
+// kernel is bound by HBM latency, so 32-row tiles stream into four LDS stages by
+// direct-to-LDS loads (partial_issue: up to three tiles in flight while one is reduced,
+// one barrier per tile) and the W^T operand stays in registers. Every tile is reduced by
+// partial_tile (partial_bf16.h), with the operand values and MFMA chain order of the
+// single-launch step's fold (segment_sums): the two produce the same bits.
 constexpr int kPStages = 4;
-constexpr int kPKRow = 272;                   // K row: 256 B + 16 B pad (17 slots of 16 B)
-constexpr int kPVRow = 288;                   // V row: 256 B + 32 B pad (18 slots)
-constexpr int kPInsts = 9;                    // 1 KB DMA instructions per tile and tensor
-constexpr int kPRegion = kPInsts * 1024;      // 9 KB each for K and V
-constexpr int kPStage = 2 * kPRegion;         // 18 KB
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Wait until this wave's loads of all but its `pending` latest tiles have landed: waves 0, 1
-// issue 5 of a tile's 18 instructions, waves 2, 3 issue 4.
-__device__ __forceinline__ void wait_tiles(int pending, int wave) {
-  if (wave < 2) {
-    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
-    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-  } else {
-    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
-    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-  }
-}
 
 // two workgroups per CU; F = 256 (two feature blocks per wave) needs the registers of one
 constexpr int partial_min_blocks(int F) { return F > 128 ? 1 : 2; }
@@ -50,7 +27,8 @@ state_partial_bf16_kernel(StateArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStage];
   static_assert(F * 256 <= kPStages * kPStage, "W^T staging exceeds the tile stages");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seg = blockIdx.x % a.n_seg;
   const int bh = blockIdx.x / a.n_seg;
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.Wk) +
@@ -59,13 +37,9 @@ state_partial_bf16_kernel(StateArgs a) {
   __syncthreads();
   constexpr int PW = FBlocks<F>::per_wave;
   const bool active = wave < FBlocks<F>::total;
-  bf16x8 wf[PW][8];   // B operand of U = K W: W^T rows 32 fb + l % 32, d = 16 s + 8 (l / 32) ..
+  bf16x8 wf[PW][8];
 #pragma unroll
-  for (int p = 0; p < PW; ++p)
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      wf[p][s] = as_bf16x8(lds_read16(smem, ktile_off(32 * (wave + 4 * p) + (lane & 31),
-                                                      2 * s + (lane >> 5))));
+  for (int p = 0; p < PW; ++p) partial_wt_frags(wf[p], smem, wave + 4 * p, lane);
   __syncthreads();   // the stages may now overwrite W^T
 
   // this segment's rows: wholly in segment A or wholly in segment B (the host's layout)
@@ -74,40 +48,13 @@ state_partial_bf16_kernel(StateArgs a) {
   const bool in_a = r0 < a.na;
   const int64_t row0 = in_a ? head_off(bh, a.a_rows, kDim) + (a.a_row0 + r0) * kDim
                             : head_off(bh, a.b_rows, kDim) + (a.b_row0 + r0 - a.na) * kDim;
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const uint16_t*>(in_a ? a.ka : a.kb) + row0), (short)0,
-      nrows * 256, kBufWord3);
-  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const uint16_t*>(in_a ? a.va : a.vb) + row0), (short)0,
-      nrows * 256, kBufWord3);
+  const i32x4 kr =
+      rsrc_words(reinterpret_cast<const uint16_t*>(in_a ? a.ka : a.kb) + row0, nrows * 256);
+  const i32x4 vr =
+      rsrc_words(reinterpret_cast<const uint16_t*>(in_a ? a.va : a.vb) + row0, nrows * 256);
   const int ntiles = (nrows + kPRows - 1) / kPRows;
-  // tile t into stage t % 4: K slot u of the 9 KB region holds row u / 17, chunk u % 17 (the
-  // pad slot copies chunk 0; slots past 32 rows hold rows of the next tile, unused); V slot u
-  // holds row u / 18, chunk u % 18 (pad slots 16, 17 copy chunk 0). Rows past the segment
-  // come back as zeros.
-  auto issue = [&](int t) {
-    unsigned char* st = smem + (t % kPStages) * kPStage;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int j = wave + 4 * i;
-      if (j < kPInsts) {
-        const int u = 64 * j + lane;
-        const int r = u / 17;
-        int c = u - 17 * r;
-        c = c == 16 ? 0 : c;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st + j * 1024), 16,
-                                                 (t * kPRows + r) * 256 + c * 16, 0, 0, 0);
-      } else if (j < 2 * kPInsts) {
-        const int jj = j - kPInsts;
-        const int u = 64 * jj + lane;
-        const int r = u / 18;
-        int c = u - 18 * r;
-        c = c >= 16 ? 0 : c;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kPRegion + jj * 1024), 16,
-                                                 (t * kPRows + r) * 256 + c * 16, 0, 0, 0);
-      }
-    }
-  };
+  const unsigned sl = lds_addr(smem);
+  const int per_tile = partial_insts<4>(wave);
 
   f32x16 acc[PW][4];
   float zp[PW];
@@ -119,63 +66,23 @@ state_partial_bf16_kernel(StateArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[p][db][i] = 0.0f;
   }
-  for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
-  const int arow = kappa(lane & 31);
+  for (int t = 0; t < kPStages - 1 && t < ntiles; ++t)
+    partial_issue<4>(kr, vr, sl + (t % kPStages) * kPStage, t, wave, lane);
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
-    const int later = ntiles - 1 - t;           // tiles issued after t, up to two in flight
-    wait_tiles(later < 2 ? later : 2, wave);
+    // tiles issued after t: up to kPStages - 2 in flight beyond it
+    const int later = ntiles - 1 - t;
+    wait_vmcnt((later < kPStages - 2 ? later : kPStages - 2) * per_tile);
     __syncthreads();   // tile t landed everywhere; the stage of tile t - 1 is free
-    if (!active) {
-      if (t + 3 < ntiles) issue(t + 3);
-      continue;
-    }
+    if (t + kPStages - 1 < ntiles)
+      partial_issue<4>(kr, vr, sl + ((t + kPStages - 1) % kPStages) * kPStage,
+                       t + kPStages - 1, wave, lane);
+    if (!active) continue;
     const unsigned char* kt = smem + (t % kPStages) * kPStage;
-    const unsigned char* vt = kt + kPRegion;
-    const int key0 = t * kPRows;
 #pragma unroll
-    for (int p = 0; p < PW; ++p) {
-      f32x16 U;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) U[i] = 0.0f;
-      bf16x8 kf[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        kf[s] = as_bf16x8(lds_read16(kt, arow * kPKRow + (2 * s + (lane >> 5)) * 16));
-#pragma unroll
-      for (int s = 0; s < 8; ++s) U = mfma32(kf[s], wf[p][s], U);
-      bf16x8 Pk[2];
-      float zsum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i0 = 8 * j + 2 * e;
-          const int key = key0 + cidx(i0, lane);
-          float u0 = U[i0] * a.u_scale, u1 = U[i0 + 1] * a.u_scale;
-          float p0 = (key < nrows) ? 1.0f + u0 + 0.5f * u0 * u0 : 0.0f;
-          float p1 = (key + 1 < nrows) ? 1.0f + u1 + 0.5f * u1 * u1 : 0.0f;
-          unsigned w = pack_bf16_u32(p0, p1);
-          zsum += bf16_lo(w) + bf16_hi(w);
-          pk[e] = w;
-        }
-        Pk[j] = as_bf16x8(pk);
-      }
-      zp[p] += zsum;
-      bf16x8 vf[4][2];
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) vf[db][j] = frag_tr(vt, kPVRow, 16 * j, 32 * db, lane);
-      // tile t + 3 goes out only now: the compiler makes a transposing LDS read wait for
-      // every load in flight, so loads issued before these reads would be waited for here
-      if (p == 0 && t + 3 < ntiles) issue(t + 3);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[p][db] = mfma32(Pk[j], vf[db][j], acc[p][db]);
-    }
+    for (int p = 0; p < PW; ++p)
+      partial_tile<4>(kt, kt + kPRegion, wf[p], t * kPRows, nrows, a.u_scale, 0, lane, acc[p],
+                      zp[p]);
   }
   if (!active) return;
   const int E = F * kDim + F;
@@ -554,9 +461,9 @@ phi_mlp_bf16_kernel(const uint16_t* __restrict__ x, int64_t n, const uint16_t* _
     // whole-row loads of tile t: piece u = 64 i + lane is row u/16, 16-byte chunk u%16; the
     // buffer descriptor's range (the head's n rows) turns rows past the end into zeros
     const __amdgpu_buffer_rsrc_t xr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)xh, (short)0, (int)(n * kDim * 2), kBufWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)xh, (short)0, (int)(n * kDim * 2), kBufRsrcWord3);
     const __amdgpu_buffer_rsrc_t orr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)oh, (short)0, (int)(n * F * 2), kBufWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)oh, (short)0, (int)(n * F * 2), kBufRsrcWord3);
     auto load_rows = [&](int64_t t, u32x4* xg) {
       const int base = (int)(t - tb) * 32 * kDim * 2 + 16 * lane;
 #pragma unroll

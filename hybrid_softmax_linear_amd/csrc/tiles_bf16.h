@@ -108,6 +108,58 @@ __device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int ld, int
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// ---- direct-to-LDS buffer loads ------------------------------------------------------
+constexpr int kBufRsrcWord3 = 0x00020000;   // gfx9 buffer descriptor word 3 (raw, 32-bit data)
+typedef int i32x4 __attribute__((ext_vector_type(4)));   // buffer descriptor words
+typedef __attribute__((address_space(3))) void lds_ptr_void;
+
+// Buffer descriptor words of [base, base + bytes) (raw buffer, stride 0).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xffffu), bytes, kBufRsrcWord3};
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(lds_ptr_void*)p;
+}
+
+// One direct-to-LDS buffer load (16 bytes per lane into lds + 16 lane; bytes past the
+// descriptor's range read as zero), written in asm so that the compiler does not track it:
+// the compiler makes the first transposing LDS read after a direct-to-LDS load it knows of
+// wait for every such load in flight. Callers order these loads themselves (vmcnt waits
+// before the barrier that hands a stage over). The load has no register result; M0
+// carries the LDS address.
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most n (0 .. 15, wave-uniform) of this wave's vector memory operations are
+// outstanding.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+  }
+}
+
 // Stage W^T for features [f0, f0+nf) into LDS as [nf][128 d] rows of 256 B, in the K-tile
 // layout (row f, chunk c at c ^ kappa(f & 15)). W is [128 d][F] bf16 (row-major).
 __device__ __forceinline__ void stage_wt(unsigned char* dst, const uint16_t* W, int F, int f0,
