@@ -13,6 +13,8 @@
 
 namespace rehyat {
 hipError_t launch_attn_bf16(const AttnArgs& a, int F, hipStream_t stream);
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream);
+bool attn_bf16_persistent(int nblocks);
 hipError_t launch_step_bf16(const AttnArgs& a, const StepArgs& s, int F, hipStream_t stream);
 int attn_bf16_tile_rows();
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int F, hipStream_t stream);
@@ -160,6 +162,8 @@ hipError_t launch_phi_rows(const rehyat_desc* d, const void* x, int64_t n, const
   return launch_phi_map_bf16(d->phi_kind, x, n, W, d->w_per_head, d->H, d->phi_hidden,
                              d->phi_parts, d->B * d->H, d->F, out, s);
 }
+
+constexpr size_t kQueueBytes = 256;   // work counters of the persistent attention launch
 
 size_t state_elems(const rehyat_desc* d) { return (size_t)d->F * d->D + d->F; }
 
@@ -368,7 +372,9 @@ size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* d) {
   // maps evaluated ahead: phi(k) and phi(q) rows of the whole sequence
   const size_t phis = (phi_ahead(d) && n_chunks(d) > 1)
                           ? 2 * phi_rows_bytes(d, (int64_t)d->T * d->HW) : 0;
-  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + imgs + phis;
+  // bf16: the persistent attention launch's work counters
+  const size_t queue = d->dtype == REHYAT_BF16 ? kQueueBytes : 0;
+  return BH * ((size_t)d->T + n_chunks(d)) * state_elems(d) * sizeof(float) + imgs + phis + queue;
 }
 
 rehyat_status rehyat_hybrid_fwd(const rehyat_desc* d, const void* q, const void* k, const void* v,
@@ -479,6 +485,12 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
   fill_tiles(a, d, nch, (int)(N - (int64_t)(nch - 1) * Np));
   a.logit_scale = kLog2e / std::sqrt((float)d->D);
   a.u_scale = us;
+  if (bf16 && attn_bf16_persistent(a.nblocks)) {
+    // the work counters of the persistent launch, the last kQueueBytes of the workspace
+    a.queue = reinterpret_cast<unsigned*>(reinterpret_cast<unsigned char*>(ws) + need - kQueueBytes);
+    hipError_t e = launch_zero_u32(a.queue, kAttnQueues, s);
+    if (e != hipSuccess) return hip_status(e, "queue reset launch");
+  }
   return hip_status(launch_attention(d, a, s), "attention launch");
 }
 

@@ -744,14 +744,51 @@ __device__ __forceinline__ int attention_block(const AttnArgs& a, int b, unsigne
   return g.bh;
 }
 
-template <int F>
+// The next query tile for a persistent workgroup on XCD home: block indices b = x + 8 j of
+// queue x are the blocks the hardware would have placed on XCD x (tile_of_block keeps a
+// window's tiles on one XCD), taken in order from the home queue, then from the others
+// once it is empty. -1: no work left.
+__device__ __forceinline__ int next_tile(unsigned* queue, int nblocks, int home) {
+  for (int k = 0; k < kAttnQueues; ++k) {
+    const int x = (home + k) & (kAttnQueues - 1);
+    const unsigned j = atomicAdd(queue + x, 1u);
+    const int64_t b = x + (int64_t)kAttnQueues * j;
+    if (b < nblocks) return (int)b;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ int xcd_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & (kAttnQueues - 1));
+}
+
+// One query tile per workgroup, or (kPersistent, a.queue set) one workgroup per compute
+// unit taking tiles from per-XCD queues until none is left: the tail of the launch then
+// balances over every XCD instead of ending with the XCD that drew the most work. Two
+// kernels, so that the loop's registers do not weigh on the one-tile form.
+template <int F, bool kPersistent>
 __global__ void __launch_bounds__(NT)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 hybrid_attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
   __shared__ float zs[F];
   __shared__ int bad_flag;
-  attention_block<F, false, false>(a, blockIdx.x, smem, zs, bad_flag);
+  if (!kPersistent) {
+    attention_block<F, false, false>(a, blockIdx.x, smem, zs, bad_flag);
+    return;
+  }
+  __shared__ int tile_s;
+  const int home = xcd_id();
+  for (;;) {
+    if (threadIdx.x == 0) tile_s = next_tile(a.queue, a.nblocks, home);
+    __syncthreads();
+    const int b = tile_s;
+    __syncthreads();   // every thread holds b before thread 0 may take the next tile
+    if (b < 0) break;
+    attention_block<F, false, false>(a, b, smem, zs, bad_flag);
+  }
 }
 
 // ---- single-launch recurrent step ------------------------------------------------------
@@ -943,12 +980,46 @@ hipError_t launch_step_bf16(const AttnArgs& a, const StepArgs& s, int F, hipStre
   return hipGetLastError();
 }
 
+// Compute units of the current device (one persistent attention workgroup each).
+static int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Query tiles per compute unit from which the persistent launch is used: with fewer, the
+// hardware's own dispatch was faster (the 21x20x30 workload, 2.6 tiles per unit, lost
+// 1.7 %; 12.5 and 14.1 tiles per unit gained 1.0 % and 3.9 %).
+constexpr int kPersistentMinTiles = 4;
+
+// Whether a launch of nblocks query tiles runs persistent (then a.queue must be set).
+bool attn_bf16_persistent(int nblocks) {
+  const int cus = device_cus();
+  return cus > 0 && nblocks >= kPersistentMinTiles * cus;
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int F, hipStream_t stream) {
-  dim3 grid(a.nblocks), block(NT);
+  const dim3 grid(a.queue ? device_cus() : a.nblocks), block(NT);
+  if (grid.x == 0) return hipErrorInvalidDevice;
+  if (a.queue) {
+    switch (F) {
+      case 64:  hipLaunchKernelGGL((hybrid_attn_bf16_kernel<64, true>), grid, block, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((hybrid_attn_bf16_kernel<128, true>), grid, block, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((hybrid_attn_bf16_kernel<256, true>), grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (F) {
-    case 64:  hipLaunchKernelGGL(hybrid_attn_bf16_kernel<64>, grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(hybrid_attn_bf16_kernel<128>, grid, block, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(hybrid_attn_bf16_kernel<256>, grid, block, 0, stream, a); break;
+    case 64:  hipLaunchKernelGGL((hybrid_attn_bf16_kernel<64, false>), grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((hybrid_attn_bf16_kernel<128, false>), grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((hybrid_attn_bf16_kernel<256, false>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -115,6 +115,9 @@ __device__ __forceinline__ int64_t head_off(int bh, int64_t rows, int cols) {
 // ---------------------------------------------------------------------------------------
 
 // Hybrid attention: one workgroup per (head, chunk, query tile).
+// Work queues of the persistent bf16 attention launch: one per XCD of the chip.
+constexpr int kAttnQueues = 8;
+
 struct AttnArgs {
   const void* q;        // query rows; head bh starts at q + bh*q_rows*D
   int64_t q_rows;       // rows per head in the q / y buffers
@@ -155,6 +158,10 @@ struct AttnArgs {
   int tiles_last;       // query tiles of the last chunk handled
   int tiles_per_head;
   int nblocks;
+  // bf16 path: NULL, one workgroup per query tile; else kAttnQueues per-XCD work counters
+  // (zero before the launch) from which a grid of one workgroup per compute unit takes the
+  // query tiles
+  unsigned* queue;
   float logit_scale;    // log2(e) / sqrt(D)
   float u_scale;        // 1 / sqrt(D)
 };

@@ -67,7 +67,17 @@ copy_rows_kernel(const u32x4* __restrict__ sk, const u32x4* __restrict__ sv, u32
   dv[d] = sv[s];
 }
 
+__global__ void __launch_bounds__(64) zero_u32_kernel(unsigned* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
 }  // namespace
+
+// Zero n 32-bit words (a fill kernel: callers may capture it in a graph).
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan_states(const float* part, float* states, int F, int D, int T, int Tc,
                               int To, int nch, int bidir, int BH, hipStream_t stream) {

@@ -129,7 +129,9 @@ rehyat_status rehyat_state_update(const rehyat_desc* desc, const void* k, const 
  *           be the same buffer)
  *   y       [B, H, N, D] y_dtype (device, written)
  *   ws      device scratch of at least rehyat_hybrid_fwd_workspace(desc) bytes (per-frame
- *           partial states and the per-chunk linear-branch states).
+ *           partial states, the per-chunk linear-branch states and, for bf16, the work
+ *           counters of the attention launch, reset by the call itself); no contents are
+ *           required on entry. Two calls must not use one workspace at the same time.
  */
 size_t rehyat_hybrid_fwd_workspace(const rehyat_desc* desc);
 rehyat_status rehyat_hybrid_fwd(const rehyat_desc* desc, const void* q, const void* k,

@@ -102,8 +102,9 @@ def test_workspace_sizes():
     E = d.F * d.D + d.F
     BH = d.B * d.H
     img = d.F * 256                       # one bf16 S^T or W^T image (F rows of 128 d)
+    queue = 256                           # work counters of the persistent attention launch
     assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == (
-        BH * (d.T + d.n_chunks) * E * 4 + BH * d.n_chunks * img + img)
+        BH * (d.T + d.n_chunks) * E * 4 + BH * d.n_chunks * img + img + queue)
     gather = 2 * BH * 40 * d.D * 2        # gathered K and V windows of (Tc + To) HW = 40 rows
     assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == (
         BH * d.Tc * E * 4 + gather + BH * img + img)
@@ -269,7 +270,7 @@ def test_feature_map_workspace_sizes():
         rows = BH * d.F * 2                      # bytes of one bf16 phi row for every head
         # whole sequence: S^T images but no W^T image, phi(k) and phi(q) of all N rows
         assert L.rehyat_hybrid_fwd_workspace(ctypes.byref(d.c())) == (
-            BH * (d.T + d.n_chunks) * E * 4 + BH * d.n_chunks * img + 2 * N * rows)
+            BH * (d.T + d.n_chunks) * E * 4 + BH * d.n_chunks * img + 2 * N * rows + 256)
         # one chunk: phi(q_c) of Tc*HW rows and phi of the (Tc + To)*HW window keys
         assert L.rehyat_recurrent_step_workspace(ctypes.byref(d.c())) == (
             BH * d.Tc * E * 4 + gather + BH * img + (30 + 40) * rows)

@@ -49,6 +49,19 @@ def test_full_workload_whole_sequence(i):
     _check_rows(y_rows, ref, inp, cfg, rows, cfg.name)
 
 
+def test_bidirectional_at_21x30x52():
+    """The bidirectional form at the 21x30x52 size (B2 H12): 3192 query tiles, so the
+    attention runs as the persistent launch (one workgroup per compute unit taking tiles
+    from per-XCD queues), which the 320x480 workload with its 672 tiles does not use."""
+    cfg = syn.config(3).replace(mode="bidir")
+    inp = syn.make_inputs(cfg)
+    _, y = _fwd(cfg, inp)
+    rows = pu.sample_rows(cfg.T, cfg.HW, cfg.Tc, per_edge=16, n_random=48, seed=33)
+    y_rows = y[:, :, rows].double().cpu().numpy()
+    ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=False, rows=rows)
+    _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + " bidirectional")
+
+
 def test_c2_bidirectional_every_row():
     """The 320x480 bidirectional workload (B1 H12, 21x20x30, Tc3 To1) on every query row of
     every head: its complement linear sets and all eight query tiles per chunk (the last one
