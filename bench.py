@@ -64,6 +64,18 @@ MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 flop/clk x 2
 HBM_PEAK_GBS = 8000.0
 
 
+def attn_kernel_name(cfg, F):
+    """The bf16 attention kernel a whole-sequence launch runs: the persistent form (one
+    workgroup per compute unit) from 4 query tiles of 256 rows per compute unit."""
+    import torch
+    Np = cfg.Tc * cfg.HW
+    nch = -(-cfg.T // cfg.Tc)
+    last = cfg.T * cfg.HW - (nch - 1) * Np
+    tiles = cfg.B * cfg.H * ((nch - 1) * (-(-Np // 256)) + -(-last // 256))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return f"hybrid_attn_bf16_kernel<{F}, {'true' if tiles >= 4 * cus else 'false'}>"
+
+
 def flop_model(B, H, T, HW, D, F, Tc, To, causal=True, phi_row_flop=None):
     """Algorithmic FLOPs (only what the method needs: no padding, no masked pairs).
 
@@ -598,7 +610,7 @@ def main(argv=None):
         "mfma_peak_frac": tflops / MFMA_PEAK_BF16_TFLOPS,
         "flop_per_step": total_flop,
         "step_ms_distribution": dist,
-        "roofline": {"bound": "mfma", "kernel": f"hybrid_attn_bf16_kernel<{desc.F}>",
+        "roofline": {"bound": "mfma", "kernel": attn_kernel_name(cfg, desc.F),
                      "achieved": attn_tflops, "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / MFMA_PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic() if headline and args.phi == "poly2" else None,
