@@ -62,6 +62,18 @@ def test_bidirectional_at_21x30x52():
     _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + " bidirectional")
 
 
+def test_f64_at_21x30x52():
+    """F = 64 at the 21x30x52 size (B2 H12, causal): the persistent launch's F = 64 kernel
+    (the workloads run F = 128 and 256)."""
+    cfg = syn.config(3).replace(F=64)
+    inp = syn.make_inputs(cfg)
+    _, y = _fwd(cfg, inp)
+    rows = pu.sample_rows(cfg.T, cfg.HW, cfg.Tc, per_edge=8, n_random=24, seed=64)
+    y_rows = y[:, :, rows].double().cpu().numpy()
+    ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=True, rows=rows)
+    _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + " F64")
+
+
 def test_c2_bidirectional_every_row():
     """The 320x480 bidirectional workload (B1 H12, 21x20x30, Tc3 To1) on every query row of
     every head: its complement linear sets and all eight query tiles per chunk (the last one
