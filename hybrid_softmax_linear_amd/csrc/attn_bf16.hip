@@ -800,8 +800,9 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 //     window reaches, two frames at a time (one per half of the workgroup; at F = 256 one
 //     frame split over the halves) with the state kernel's operand values and MFMA order,
 //     and adds them onto S, z in frame order, exactly as the fold kernel does, into a
-//     workspace copy xs. It also writes the chunk's last To frames to
-//     the new tail, a buffer apart from the carried one.
+//     workspace copy xs. The chunk's last To frames go to the new tail, a buffer apart from
+//     the carried one: copied by the grid's padding workgroups (the fold workgroups are
+//     padded to a multiple of 8), or by the fold workgroups when there are none.
 //   * Every workgroup of a head reports to the head's counter (an agent-scope atomic add)
 //     once its reads of S, z and the carried tail have returned; the one that completes the
 //     count is the only one left that could read S and z, and copies xs into them.
@@ -815,13 +816,46 @@ hybrid_attn_bf16_kernel(AttnArgs a) {
 // each workgroup consumes their values before the barrier ahead of its add, and the last
 // workgroup stores only after its add has returned the final count.
 
+// The new tail of head bh: the chunk's last trow rows of K and V (16-byte units, four per
+// tensor in flight per thread).
+__device__ __forceinline__ void copy_tail(const StepArgs& s, int bh, int tid) {
+  const int64_t units = s.trow * (kDim * 2 / 16);
+  const u32x4* kc = reinterpret_cast<const u32x4*>(s.kc) +
+                    ((int64_t)bh * s.crow + (s.crow - s.trow)) * (kDim * 2 / 16);
+  const u32x4* vc = reinterpret_cast<const u32x4*>(s.vc) +
+                    ((int64_t)bh * s.crow + (s.crow - s.trow)) * (kDim * 2 / 16);
+  u32x4* kt = reinterpret_cast<u32x4*>(s.ktail) + (int64_t)bh * units;
+  u32x4* vt = reinterpret_cast<u32x4*>(s.vtail) + (int64_t)bh * units;
+#pragma unroll 1
+  for (int64_t u0 = tid; u0 < units; u0 += 4 * NT) {
+    u32x4 kx[4], vx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t u = u0 + (int64_t)j * NT;
+      if (u < units) {
+        kx[j] = kc[u];
+        vx[j] = vc[u];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t u = u0 + (int64_t)j * NT;
+      if (u < units) {
+        kt[u] = kx[j];
+        vt[u] = vx[j];
+      }
+    }
+  }
+}
+
 // The fold workgroup of head bh: xs = ((S + p_0) + p_1) + ... over the nseg frames (S taken
-// as 0 for the first chunk), then the new tail. Each round the two halves of the workgroup
+// as 0 for the first chunk), then (copy) the new tail. Each round the two halves of the workgroup
 // form two frames' partials (F <= 128) or the two halves of one frame's (F = 256, whose
 // two feature blocks per wave would not fit beside the attention code's registers) and
 // store them (pp: [2][F*D + F]); then all threads add them on elementwise, in frame order.
 template <int F>
-__device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned char* smem, int tid) {
+__device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned char* smem, int tid,
+                                          bool copy) {
   constexpr int E = F * kDim + F;
   constexpr bool kSplit = F > 128;
   constexpr int kPer = kSplit ? 1 : 2;   // frames per round
@@ -880,35 +914,10 @@ __device__ __forceinline__ void fold_head(const StepArgs& s, int bh, unsigned ch
     }
     __syncthreads();   // pp free for the next round
   }
-  // the new tail: the chunk's last trow rows (16-byte units, four in flight per thread)
-  const int64_t units = s.trow * (kDim * 2 / 16);
-  const u32x4* kc = reinterpret_cast<const u32x4*>(s.kc) +
-                    ((int64_t)bh * s.crow + (s.crow - s.trow)) * (kDim * 2 / 16);
-  const u32x4* vc = reinterpret_cast<const u32x4*>(s.vc) +
-                    ((int64_t)bh * s.crow + (s.crow - s.trow)) * (kDim * 2 / 16);
-  u32x4* kt = reinterpret_cast<u32x4*>(s.ktail) + (int64_t)bh * units;
-  u32x4* vt = reinterpret_cast<u32x4*>(s.vtail) + (int64_t)bh * units;
-#pragma unroll 1
-  for (int64_t u0 = tid; u0 < units; u0 += 4 * NT) {
-    u32x4 kx[4], vx[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t u = u0 + (int64_t)j * NT;
-      if (u < units) {
-        kx[j] = kc[u];
-        vx[j] = vc[u];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t u = u0 + (int64_t)j * NT;
-      if (u < units) {
-        kt[u] = kx[j];
-        vt[u] = vx[j];
-      }
-    }
-  }
+  // the new tail, unless the grid's padding workgroups copy it
+  if (copy) copy_tail(s, bh, tid);
 }
+
 
 // The last workgroup of head bh: S, z <- xs (or 0 for a first chunk with nothing folded).
 template <int F>
@@ -940,9 +949,15 @@ recurrent_step_bf16_kernel(AttnArgs a, StepArgs s) {
   const int BH = a.nblocks / a.tiles_per_head;
   int bh;
   if (b < s.fold_blocks) {
-    if (b >= BH) return;   // padding block: reports nowhere
+    if (b >= BH) {
+      // padding workgroup (the fold workgroups are padded to a multiple of 8): copies the new
+      // tails of heads b - BH, b - BH + P, ... (P padding workgroups), which takes the copy
+      // off the fold workgroups; reports nowhere
+      for (int h = b - BH; h < BH; h += s.fold_blocks - BH) copy_tail(s, h, tid);
+      return;
+    }
     bh = b;
-    fold_head<F>(s, bh, smem, tid);
+    fold_head<F>(s, bh, smem, tid, s.fold_blocks == BH);
   } else {
     bh = attention_block<F, true, true>(a, b - s.fold_blocks, smem, zs, bad_flag);
   }
