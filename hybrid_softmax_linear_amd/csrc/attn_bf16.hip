@@ -88,6 +88,13 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // (16 consecutive rows, one chunk) cover all 64 banks, and every fragment read below is one
 // per-lane base plus a constant offset. V row r at r * 288 (see kVRow).
 
+// Descriptor of the rows from byte t0 on: base advanced by t0, range shortened by t0.
+__device__ __forceinline__ i32x4 rsrc_from(i32x4 r, int t0) {
+  const uint64_t b = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + (uint32_t)t0;
+  const int left = r[2] - t0;
+  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), left > 0 ? left : 0, r[3]};
+}
+
 // Issue the direct-to-LDS loads of tile kt into one stage. Each instruction writes 64
 // consecutive 16-byte slots (1 KB) of a tile; for K slot u holds row u / 17, chunk u % 17
 // (the pad slot, chunk 16, takes a second copy of chunk 0); for V row u / 18, chunk u % 18
@@ -98,6 +105,14 @@ template <bool kSplit, int kPart = 2>
 __device__ __forceinline__ void tile_dma_from(i32x4 k, i32x4 v, const Src& s, int kt,
                                               unsigned char* stage, int wave, int lane) {
   const unsigned sl = lds_addr(stage);
+  if (!kSplit) {
+    // descriptors that start at the tile: the lanes' offsets are the same for every tile, and
+    // the advance is scalar work (rows past the window still read as zeros)
+    const int t0 = kt * kKeys * 256;
+    if (kPart != 1) k = rsrc_from(k, t0);
+    if (kPart != 0) v = rsrc_from(v, t0);
+    kt = 0;
+  }
 #pragma unroll
   for (int i = 0; i < (kPart == 1 ? 0 : (kDmaInsts + NW - 1) / NW); ++i) {
     const int j = wave + NW * i;
