@@ -202,7 +202,8 @@ def bench_stream(args):
     """One line for streaming: 27 recurrent steps over the 81x30x52 latent (B1 H12, Tc3 To1),
     each step's q, k, v chunk resident in HBM; a pass is the 27 steps, each one launch of
     rehyat_recurrent_step_fused. Context: the same pass with rehyat_recurrent_step (seven
-    launches per step)."""
+    launches per step), and the pass with each chunk copied from pinned host memory before
+    its step (PCIe-inclusive; the copies alone are timed too)."""
     import torch
     import synthetic as syn
     import hybrid_softmax_linear_amd as hs
@@ -238,6 +239,31 @@ def bench_stream(args):
 
     ms, step_ms, n = timed(True, 4)
     ms_multi, attn_ms_multi, _ = timed(False, 1)
+
+    # PCIe-inclusive pass: each chunk copied from pinned host memory into fixed device
+    # buffers before its step, on the same stream (context only; inputs are not resident)
+    host = [tuple(x.cpu().pin_memory() for x in c) for c in chunks]
+    bufs = tuple(torch.empty_like(x) for x in chunks[0])
+    rec = ta.Recurrent(cfg.B, cfg.H, cfg.D, cfg.F, T=cfg.T, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To,
+                       device=dev, fused=True)
+
+    def h2d_pass(with_step=True):
+        rec.t = 0
+        for hc in host:
+            for b, h in zip(bufs, hc):
+                b.copy_(h, non_blocking=True)
+            if with_step:
+                rec.step(*bufs, W, out=yc)
+
+    for _ in range(2):
+        h2d_pass()
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    ms_h2d = time_calls(h2d_pass, max(3, args.steps // 4), 0)
+    ms_copy = time_calls(lambda: h2d_pass(False), max(3, args.steps // 4), 0)
+    free1 = torch.cuda.mem_get_info()[0]
+    chunk_bytes = sum(x.numel() * x.element_size() for x in chunks[0])
+    del host, bufs, rec
     total, attn_total = flop_model(cfg.B, cfg.H, cfg.T, cfg.HW, cfg.D, cfg.F, cfg.Tc, cfg.To)[:2]
     per_launch = total / steps
     result = {
@@ -265,7 +291,12 @@ def bench_stream(args):
                     "multi_launch_ms_per_step": ms_multi / steps,
                     "multi_launch_attention_kernel_ms": attn_ms_multi,
                     "multi_launch_attention_tflops": attn_total / steps / (attn_ms_multi * 1e-3) / 1e12,
-                    "single_over_multi_launch_speedup": ms_multi / ms},
+                    "single_over_multi_launch_speedup": ms_multi / ms,
+                    "pcie_inclusive_ms_per_step": ms_h2d / steps,
+                    "pcie_inclusive_tokens_per_s": cfg.B * cfg.N / (ms_h2d * 1e-3),
+                    "h2d_copy_ms_per_step": ms_copy / steps,
+                    "h2d_copy_GB_per_s": chunk_bytes / (ms_copy / steps * 1e-3) / 1e9,
+                    "device_free_bytes_change_over_pcie_passes": free1 - free0},
     }
     print(json.dumps(result))
     return 0

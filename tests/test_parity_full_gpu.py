@@ -137,8 +137,8 @@ def test_full_workload_recurrent_equals_whole(i, fused):
 def test_streaming_81_frames_flat_memory(fused):
     """27 recurrent steps over the 81-frame latent (rehyat_recurrent_step, or
     rehyat_recurrent_step_fused): host chunks are copied into fixed device buffers, device
-    memory stays flat, outputs match the oracle on sampled rows and the whole-sequence form
-    bitwise."""
+    memory stays flat (torch's allocator and the device's free memory, hipMemGetInfo), outputs
+    match the oracle on sampled rows and the whole-sequence form bitwise."""
     cfg = syn.config(4)
     inp = syn.make_inputs(cfg)
     B, H, D, Np = cfg.B, cfg.H, cfg.D, cfg.Tc * cfg.HW
@@ -166,11 +166,13 @@ def test_streaming_81_frames_flat_memory(fused):
         streamed[:, :, r0:r1].copy_(y_c)
         y_host.copy_(y_c)
         torch.cuda.synchronize()
-        mem.append((torch.cuda.memory_allocated(), torch.cuda.max_memory_allocated()))
+        mem.append((torch.cuda.memory_allocated(), torch.cuda.max_memory_allocated(),
+                    torch.cuda.mem_get_info()[0]))
         for r in rows_by_chunk.get(t, []):
             got[r] = y_host[:, :, r - r0].double().numpy()
     assert len(set(m[0] for m in mem)) == 1, f"device memory not flat: {mem}"
     assert len(set(m[1] for m in mem)) == 1, f"peak device memory grew: {mem}"
+    assert len(set(m[2] for m in mem)) == 1, f"device free memory (hipMemGetInfo) moved: {mem}"
     y_rows = np.stack([got[r] for r in rows], axis=2)
     ref = pu.oracle_rows(inp, HW=cfg.HW, Tc=cfg.Tc, To=cfg.To, causal=True, rows=rows)
     _check_rows(y_rows, ref, inp, cfg, rows, cfg.name + (" streamed, one launch per step"
