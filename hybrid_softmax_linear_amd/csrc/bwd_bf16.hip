@@ -23,6 +23,7 @@
 #include "common.h"
 #include "tiles_bf16.h"
 
+
 namespace rehyat {
 namespace {
 
@@ -498,53 +499,69 @@ bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// ---- dk, dv: one workgroup of 4 waves per 128 keys of a chunk, lane = key ----------------
+// ---- dk, dv: one workgroup of 8 waves per 128 keys of a chunk, lane = key ----------------
 //
 // Window part: for every chunk whose window holds the keys (the keys' own chunk and the
 // next ones whose overlap reaches back to them), per 32-query block: S = Q K^T and
 // dP = dY V^T (rows of Q and dY in kappa order, so the results are B operands over
-// queries), p and ds, dv^T += dY^T p, dk^T += Q^T ds (transposing LDS reads). The kernel
-// runs one wave per SIMD (K, V fragments and both accumulators live in registers), so
-// nothing hides a wave's own latencies: 128-query tiles are double-buffered, each block's
-// LDS fragments are read as one batch, and the S, dP MFMAs of two blocks run ahead of
-// their exponentials. Linear part,
+// queries), p and ds, dv^T += dY^T p, dk^T += Q^T ds (transposing LDS reads). Linear part,
 // per key frame present in the tile: U^T = W^T K^T, (G v)^T, phi(k), dphi(k) = G v - h,
 // gk = dphi (1 + u) / sqrt(D), dv^T += G^T phi(k)^T, dk^T += W gk^T, for the lanes whose key
 // lies in that frame.
-constexpr int kKW = 4;                                    // waves of the dk/dv kernel
-constexpr int kQTile = 128;
+// The workgroup's 128 keys of K and V stay in LDS (rows of 256 B padded to 272, read as
+// B-operand pieces each block) rather than in registers, which lets two waves share a
+// SIMD: waves w and w + 4 take the same 32 keys; 64-query tiles (Q, dY, lse and dy.y by
+// direct-to-LDS loads) are double-buffered and wave w takes the first 32-query block of
+// each, wave w + 4 the second; in the linear part they take alternate 32-feature blocks.
+// Each holds partial dk and dv sums, added through LDS at the end (wave w finishes dk,
+// wave w + 4 dv).
+constexpr int kKW = 8;
 using QL = Swz256;                                        // layout of the Q and dY tiles
+constexpr int kQTile = 64;
 constexpr int kQBuf = 2 * kQTile * QL::kRow + 2 * kQTile * 4;   // Q, dY rows; lse, dy.y
-constexpr int kDkLds = kLinLds > 2 * kQBuf ? kLinLds : 2 * kQBuf;
+constexpr int kKV = 2 * 128 * kRowB;                               // K, V of the 128 keys
+constexpr int kRed = 2 * 4 * 64 * 64 * 4;                          // partial dk, dv exchange
+constexpr int kDkWin = 2 * kQBuf + kKV;
+constexpr int kDkLin = kLinLds > kRed ? kLinLds : kRed;
+constexpr int kDkLds = kDkWin > kDkLin ? kDkWin : kDkLin;
 
 template <int F>
 __global__ void __launch_bounds__(64 * kKW)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
   constexpr int FS = F < 128 ? F : 128;
   constexpr int RW = 2 * FS + 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kDkLds];
   __shared__ float hs[F];
-  // the wave index is uniform: held in a scalar register, the tile loads' LDS addresses are
-  // scalar too and free vector registers for the loop
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;                               // key group (32 keys)
+  const int half = wave >> 2;                            // 0: first block of a tile, 1: second
   int kt;
   const BwdGeo g = bwd_geo(a, blockIdx.x, kt);
-  const int kw0 = kt * 128 + wave * 32;                  // first key of the wave in the chunk
+  const int kw0 = kt * 128 + kg * 32;                    // first key of the group in the chunk
   const bool active = kw0 < g.rows;
   const int kl = kw0 + (lane & 31);
   const bool ok = active && kl < g.rows;
   const int64_t key = g.row0 + (ok ? kl : 0);            // this lane's key row
   const int64_t hrow = (int64_t)g.bh * a.N;
-  bf16x8 Kf[8], Vf[8];
+  unsigned char* sK = smem + 2 * kQBuf;                 // K rows of the 128 keys (272 B)
+  unsigned char* sV = sK + 128 * kRowB;
   {
-    const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k) + (hrow + key) * kDim + 8 * (lane >> 5);
-    const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v) + (hrow + key) * kDim + 8 * (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      Kf[s] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(kp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
-      Vf[s] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(vp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
+    // K, V rows of the tile's keys (zero past the chunk)
+    const int nkeys = g.rows - kt * 128 < 128 ? g.rows - kt * 128 : 128;
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + (hrow + g.row0 + kt * 128) * kDim;
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + (hrow + g.row0 + kt * 128) * kDim;
+    for (int u = tid; u < 128 * 16; u += 64 * kKW) {
+      const int r = u >> 4, c = u & 15;
+      const bool in = r < nkeys;
+      const u32x4 kx = in ? *reinterpret_cast<const u32x4*>(kb + r * kDim + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vx = in ? *reinterpret_cast<const u32x4*>(vb + r * kDim + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK + r * kRowB + 16 * c) = kx;
+      *reinterpret_cast<u32x4*>(sV + r * kRowB + 16 * c) = vx;
     }
   }
+  // this lane's B-operand pieces: key row 32 kg + l mod 32, chunk 2 s + l / 32
+  const int kvoff = (32 * kg + (lane & 31)) * kRowB + 16 * (lane >> 5);
   f32x16 dK[4], dV[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -555,10 +572,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int64_t Np = (int64_t)a.Tc * a.HW;
   const int64_t tile_end = g.row0 + (kt * 128 + 128 < g.rows ? kt * 128 + 128 : g.rows);
 
-  // ---- window part: the key's own chunk and later chunks whose window reaches back ----
-  // Query tiles (chunk tq, rows q0 .. q0 + kQTile) are double-buffered: tile n + 1's Q, dY,
-  // lse and dy.y rows stream into the other buffer by direct-to-LDS loads while tile n is
-  // reduced. Rows past the chunk come back as zeros (Q = dY = 0 makes every term zero).
+  // ---- window part ----
   auto chunk_lo = [&](int tq) {
     const int64_t r = tq * Np - (int64_t)a.To * a.HW;
     return r > 0 ? r : (int64_t)0;
@@ -578,17 +592,14 @@ bwd_dkdv_kernel(BwdArgs a) {
         (void*)(a.dyb + (hrow + r0) * kDim), (short)0, bytes, kBufWord3);
     dma_tile<QL, kQTile, kKW>(qr, base, wave, lane);
     dma_tile<QL, kQTile, kKW>(yr, base + kQTile * QL::kRow, wave, lane);
-    // lse and dy.y of the tile: 4 bytes per lane, one instruction per 64 rows each
     const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.lse + hrow + r0), (short)0, bytes / 64, kBufWord3);
     const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.dvec + hrow + r0), (short)0, bytes / 64, kBufWord3);
-    if (wave < kQTile / 64) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          lr, (lds_void*)(base + 2 * kQTile * QL::kRow + wave * 256), 4, (wave * 64 + lane) * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          dr, (lds_void*)(base + 2 * kQTile * QL::kRow + kQTile * 4 + wave * 256), 4,
-          (wave * 64 + lane) * 4, 0, 0, 0);
+    if (wave == 0) {
+      unsigned char* st = base + 2 * kQTile * QL::kRow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void*)st, 4, lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + kQTile * 4), 4, lane * 4, 0, 0, 0);
     }
   };
   int tq = g.t, q0 = 0, qbuf = 0;
@@ -603,7 +614,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
     const bool nhave = ntq < a.n_chunks && chunk_lo(ntq) < tile_end;
     wait_vmem_all();
-    __syncthreads();   // tile landed everywhere; the other buffer's last reader is done
+    __syncthreads();   // tile landed everywhere (and K, V staged); the other buffer is free
     if (nhave) issue(ntq, nq0, qbuf ^ 1);
     const unsigned char* sQ = smem + qbuf * kQBuf;
     const unsigned char* sY = sQ + kQTile * QL::kRow;
@@ -615,84 +626,68 @@ bwd_dkdv_kernel(BwdArgs a) {
     have = nhave;
     qbuf ^= 1;
     if (!active) continue;
-    // The tile's 32-query blocks in pairs: the S and dP MFMAs of both blocks of a pair
-    // first, then each block's p and ds (while the other block's MFMAs run) and its dv, dk
-    // MFMAs. Every block's LDS operand fragments are read as one batch before its MFMAs.
+    const int qb = half;   // this wave's 32-query block of the tile
+    f32x16 S, Pd;
 #pragma unroll
-    for (int pr = 0; pr < kQTile / 32; pr += 2) {
-      f32x16 S[2], Pd[2];
+    for (int i = 0; i < 16; ++i) S[i] = Pd[i] = 0.0f;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int qb = pr + h2;
-        bf16x8 qf[8], yf[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          qf[s] = as_bf16x8(lds_read16(sQ, QL::a_off(lane, s) + qb * 32 * QL::kRow));
-          yf[s] = as_bf16x8(lds_read16(sY, QL::a_off(lane, s) + qb * 32 * QL::kRow));
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[h2][i] = Pd[h2][i] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          S[h2] = mfma32(qf[s], Kf[s], S[h2]);
-          Pd[h2] = mfma32(yf[s], Vf[s], Pd[h2]);
-        }
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int qb = pr + h2;
-        // this lane's query statistics: element i holds query 32 qb + cidx(i, lane), two
-        // runs of 8 consecutive queries
-        f32x4 Lq[4], Dq[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qi = 32 * qb + 16 * (r >> 1) + 8 * (lane >> 5) + 4 * (r & 1);
-          Lq[r] = *reinterpret_cast<const f32x4*>(sL + qi);
-          Dq[r] = *reinterpret_cast<const f32x4*>(sD + qi);
-        }
-        bf16x8 yt[4][2], qt[4][2];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int o = (32 * qb + 16 * j) * QL::kRow;
-            yt[db][j] = frag_tr_at(sY + o + QL::t_off(lane, db, 0), sY + o + QL::t_off(lane, db, 1));
-            qt[db][j] = frag_tr_at(sQ + o + QL::t_off(lane, db, 0), sQ + o + QL::t_off(lane, db, 1));
-          }
-        bf16x8 pb[2], dsb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 pp, pd;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float p2[2], d2[2];
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-              const int i = 8 * j + 2 * e + q2;
-              const float Lv = Lq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
-              const float Dv = Dq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
-              const float p = key_in ? fast_exp2(S[h2][i] * ls - Lv) : 0.0f;
-              p2[q2] = p;
-              d2[q2] = p * (Pd[h2][i] - Dv) * us;
-            }
-            pp[e] = pack_bf16_u32(p2[0], p2[1]);
-            pd[e] = pack_bf16_u32(d2[0], d2[1]);
-          }
-          pb[j] = as_bf16x8(pp);
-          dsb[j] = as_bf16x8(pd);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            dV[db] = mfma32(yt[db][j], pb[j], dV[db]);
-            dK[db] = mfma32(qt[db][j], dsb[j], dK[db]);
-          }
-      }
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const bf16x8 qf = as_bf16x8(lds_read16(sQ, QL::a_off(lane, s2) + qb * 32 * QL::kRow));
+      const bf16x8 yf = as_bf16x8(lds_read16(sY, QL::a_off(lane, s2) + qb * 32 * QL::kRow));
+      const bf16x8 kf = as_bf16x8(lds_read16(sK, kvoff + 32 * s2));
+      const bf16x8 vf = as_bf16x8(lds_read16(sV, kvoff + 32 * s2));
+      S = mfma32(qf, kf, S);
+      Pd = mfma32(yf, vf, Pd);
     }
+    f32x4 Lq[4], Dq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = 32 * qb + 16 * (r >> 1) + 8 * (lane >> 5) + 4 * (r & 1);
+      Lq[r] = *reinterpret_cast<const f32x4*>(sL + qi);
+      Dq[r] = *reinterpret_cast<const f32x4*>(sD + qi);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 pp, pd;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p2[2], d2[2];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int i = 8 * j + 2 * e + q2;
+          const float Lv = Lq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
+          const float Dv = Dq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
+          const float p = key_in ? fast_exp2(S[i] * ls - Lv) : 0.0f;
+          p2[q2] = p;
+          d2[q2] = p * (Pd[i] - Dv) * us;
+        }
+        pp[e] = pack_bf16_u32(p2[0], p2[1]);
+        pd[e] = pack_bf16_u32(d2[0], d2[1]);
+      }
+      pb[j] = as_bf16x8(pp);
+      dsb[j] = as_bf16x8(pd);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int o = (32 * qb + 16 * j) * QL::kRow;
+        const bf16x8 yt = frag_tr_at(sY + o + QL::t_off(lane, db, 0), sY + o + QL::t_off(lane, db, 1));
+        const bf16x8 qt = frag_tr_at(sQ + o + QL::t_off(lane, db, 0), sQ + o + QL::t_off(lane, db, 1));
+        dV[db] = mfma32(yt, pb[j], dV[db]);
+        dK[db] = mfma32(qt, dsb[j], dK[db]);
+      }
   }
+  __syncthreads();   // every wave done with the tiles; K, V still in LDS
 
-  // ---- linear part: per key frame of the tile ----
+  // ---- linear part: per key frame of the tile, alternate feature blocks per wave pair ----
+  bf16x8 Kf[8], Vf[8];
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) {
+    Kf[s2] = as_bf16x8(lds_read16(sK, kvoff + 32 * s2));
+    Vf[s2] = as_bf16x8(lds_read16(sV, kvoff + 32 * s2));
+  }
   const int h = g.bh % a.H;
   const uint16_t* wt = a.wt + (a.w_per_head ? (int64_t)h * F * kDim : 0);
   const uint16_t* w = a.w + (a.w_per_head ? (int64_t)h * kDim * F : 0);
@@ -710,7 +705,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     const float* hsrc = a.st + ((int64_t)g.bh * a.nslot + fr) * ((int64_t)F * kDim + F) + F * kDim;
 #pragma unroll 1
     for (int f0 = 0; f0 < F; f0 += FS) {
-      __syncthreads();
+      __syncthreads();   // (first pass: K, V read into registers) the slabs are free
       stage_rows(sWt, kRowB, wt + (int64_t)f0 * kDim, kDim, 0, FS, kDim, tid, 64 * kKW);
       stage_rows(sG, kRowB, gimg + (int64_t)f0 * kDim, kDim, 0, FS, kDim, tid, 64 * kKW);
       stage_rows(sW, RW, w, F, f0, kDim, FS, tid, 64 * kKW);
@@ -718,14 +713,14 @@ bwd_dkdv_kernel(BwdArgs a) {
       __syncthreads();
       if (!active) continue;
 #pragma unroll 1
-      for (int fb = 0; fb < FS / 32; ++fb) {
+      for (int fb = half; fb < FS / 32; fb += 2) {
         f32x16 U, DP;
 #pragma unroll
         for (int i = 0; i < 16; ++i) U[i] = DP[i] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          U = mfma32(as_bf16x8(lds_read16(sWt, ab + fb * 32 * kRowB + 32 * s)), Kf[s], U);
-          DP = mfma32(as_bf16x8(lds_read16(sG, ab + fb * 32 * kRowB + 32 * s)), Vf[s], DP);
+        for (int s2 = 0; s2 < 8; ++s2) {
+          U = mfma32(as_bf16x8(lds_read16(sWt, ab + fb * 32 * kRowB + 32 * s2)), Kf[s2], U);
+          DP = mfma32(as_bf16x8(lds_read16(sG, ab + fb * 32 * kRowB + 32 * s2)), Vf[s2], DP);
         }
         bf16x8 psb[2], gkb[2];
 #pragma unroll
@@ -761,18 +756,39 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   }
+
+  // ---- the two partial sums of each key group: wave w finishes dk, wave w + 4 dv ----
+  __syncthreads();   // slabs no longer read
+  float* xk = reinterpret_cast<float*>(smem) + kg * 64 * 64;            // dk of wave kg + 4
+  float* xv = reinterpret_cast<float*>(smem) + (4 + kg) * 64 * 64;      // dv of wave kg
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float* dst = (half ? xk : xv) + ((db * 4 + q4) * 64 + lane) * 4;
+      const f32x16& src = half ? dK[db] : dV[db];
+      *reinterpret_cast<f32x4*>(dst) =
+          f32x4{src[4 * q4], src[4 * q4 + 1], src[4 * q4 + 2], src[4 * q4 + 3]};
+    }
+  __syncthreads();
+  f32x16 (&mine4)[4] = half ? dV : dK;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>((half ? xv : xk) + ((db * 4 + q4) * 64 + lane) * 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mine4[db][4 * q4 + c] += o[c];
+    }
   if (ok) {
-    float* ok_ = a.dx + (hrow + key) * kDim;
-    float* ov = a.dv + (hrow + key) * kDim;
+    float* out = (half ? a.dv : a.dx) + (hrow + key) * kDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const int d = 32 * db + 8 * gi + 4 * (lane >> 5);
-        *reinterpret_cast<f32x4*>(ok_ + d) =
-            f32x4{dK[db][4 * gi], dK[db][4 * gi + 1], dK[db][4 * gi + 2], dK[db][4 * gi + 3]};
-        *reinterpret_cast<f32x4*>(ov + d) =
-            f32x4{dV[db][4 * gi], dV[db][4 * gi + 1], dV[db][4 * gi + 2], dV[db][4 * gi + 3]};
+        *reinterpret_cast<f32x4*>(out + d) = f32x4{mine4[db][4 * gi], mine4[db][4 * gi + 1],
+                                                   mine4[db][4 * gi + 2], mine4[db][4 * gi + 3]};
       }
   }
 }
