@@ -100,6 +100,26 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t src, unsigned ch
   }
 }
 
+// dma_tile by loads the compiler does not track (tiles_bf16.h, dma16): no wait for them is
+// placed before later LDS reads; the caller waits (vmcnt) before the barrier that hands the
+// tile over.
+template <class L, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile_untracked(i32x4 src, unsigned dst, int wave, int lane) {
+  constexpr int kInsts = ROWS * L::kSlots / 64;
+  static_assert(ROWS * L::kSlots % 64 == 0, "whole DMA instructions");
+#pragma unroll
+  for (int i = 0; i < (kInsts + NW - 1) / NW; ++i) {
+    const int j = wave + NW * i;
+    if (j < kInsts) {
+      const int u = 64 * j + lane;
+      const int r = u / L::kSlots;
+      const int p = u - L::kSlots * r;
+      const int c = p < 16 ? p ^ L::h(r & 15) : 0;
+      dma16(src, dst + j * 1024, r * 256 + c * 16);
+    }
+  }
+}
+
 // Transposing fragment of a layout-L tile: the two reads at lo and hi (t_off(.., 0 / 1)).
 __device__ __forceinline__ bf16x8 frag_tr_at(const unsigned char* lo, const unsigned char* hi) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
@@ -414,12 +434,10 @@ bwd_dq_kernel(BwdArgs a) {
   const float ls = a.logit_scale;
   auto issue = [&](int k0, int buf) {
     const int bytes = (nk - k0) * 256;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * kDim), (short)0, bytes, kBufWord3);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * kDim), (short)0, bytes, kBufWord3);
-    dma_tile<KL, kKeyTile, kQW>(kr, sK + buf * 2 * kKeyTile * KL::kRow, wave, lane);
-    dma_tile<KL, kKeyTile, kQW>(vr, sV + buf * 2 * kKeyTile * KL::kRow, wave, lane);
+    const i32x4 kr = rsrc_words(kbase + (int64_t)k0 * kDim, bytes);
+    const i32x4 vr = rsrc_words(vbase + (int64_t)k0 * kDim, bytes);
+    dma_tile_untracked<KL, kKeyTile, kQW>(kr, lds_addr(sK + buf * 2 * kKeyTile * KL::kRow), wave, lane);
+    dma_tile_untracked<KL, kKeyTile, kQW>(vr, lds_addr(sV + buf * 2 * kKeyTile * KL::kRow), wave, lane);
   };
   __syncthreads();   // the linear part's slabs are no longer read
   issue(0, 0);
@@ -584,22 +602,15 @@ bwd_dkdv_kernel(BwdArgs a) {
   auto issue = [&](int tq, int q0, int b) {
     const int64_t r0 = tq * Np + q0;
     const int bytes = (chunk_rows(tq) - q0) * 256;
-    unsigned char* base = smem + b * kQBuf;
-    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const uint16_t*>(a.q) + (hrow + r0) * kDim), (short)0, bytes,
-        kBufWord3);
-    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.dyb + (hrow + r0) * kDim), (short)0, bytes, kBufWord3);
-    dma_tile<QL, kQTile, kKW>(qr, base, wave, lane);
-    dma_tile<QL, kQTile, kKW>(yr, base + kQTile * QL::kRow, wave, lane);
-    const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.lse + hrow + r0), (short)0, bytes / 64, kBufWord3);
-    const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.dvec + hrow + r0), (short)0, bytes / 64, kBufWord3);
+    const unsigned base = lds_addr(smem + b * kQBuf);
+    const i32x4 qr = rsrc_words(reinterpret_cast<const uint16_t*>(a.q) + (hrow + r0) * kDim, bytes);
+    const i32x4 yr = rsrc_words(a.dyb + (hrow + r0) * kDim, bytes);
+    dma_tile_untracked<QL, kQTile, kKW>(qr, base, wave, lane);
+    dma_tile_untracked<QL, kQTile, kKW>(yr, base + kQTile * QL::kRow, wave, lane);
     if (wave == 0) {
-      unsigned char* st = base + 2 * kQTile * QL::kRow;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void*)st, 4, lane * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(st + kQTile * 4), 4, lane * 4, 0, 0, 0);
+      const unsigned st = base + 2 * kQTile * QL::kRow;
+      dma4(rsrc_words(a.lse + hrow + r0, bytes / 64), st, lane * 4);
+      dma4(rsrc_words(a.dvec + hrow + r0, bytes / 64), st + kQTile * 4, lane * 4);
     }
   };
   int tq = g.t, q0 = 0, qbuf = 0;

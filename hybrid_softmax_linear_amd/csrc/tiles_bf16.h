@@ -137,6 +137,14 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
                : "memory", "m0");
 }
 
+// The same for 4 bytes per lane (into lds + 4 lane).
+__device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Wait until at most n (0 .. 15, wave-uniform) of this wave's vector memory operations are
 // outstanding.
 __device__ __forceinline__ void wait_vmcnt(int n) {
