@@ -28,8 +28,6 @@ namespace rehyat {
 namespace {
 
 constexpr int kRowB = 272;                     // LDS row of 128 bf16 + 16 B pad
-constexpr int kBufWord3 = 0x00020000;          // gfx9 buffer descriptor word 3
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
@@ -78,33 +76,14 @@ struct Swz256 {
 };
 
 // Direct-to-LDS copy of ROWS rows of 256 B (row r at byte r*256 of the buffer) into a tile
-// of layout L. Instruction j writes the 64 consecutive 16-byte slots 64j..64j+63; slot u is
-// row u / kSlots, stored chunk p = u mod kSlots, which holds chunk p ^ h(row) (pad slots
-// take a copy of chunk 0). Rows past the buffer's range read as zeros.
+// of layout L at LDS address dst. Instruction j writes the 64 consecutive 16-byte slots
+// 64j..64j+63; slot u is row u / kSlots, stored chunk p = u mod kSlots, which holds chunk
+// p ^ h(row) (pad slots take a copy of chunk 0). Rows past the buffer's range read as
+// zeros. The loads are ones the compiler does not track (tiles_bf16.h, dma16), so it places
+// no wait for them before later LDS reads: the caller waits (vmcnt) before the barrier
+// that hands the tile over.
 template <class L, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t src, unsigned char* dst, int wave,
-                                         int lane) {
-  constexpr int kInsts = ROWS * L::kSlots / 64;
-  static_assert(ROWS * L::kSlots % 64 == 0, "whole DMA instructions");
-#pragma unroll
-  for (int i = 0; i < (kInsts + NW - 1) / NW; ++i) {
-    const int j = wave + NW * i;
-    if (j < kInsts) {
-      const int u = 64 * j + lane;
-      const int r = u / L::kSlots;
-      const int p = u - L::kSlots * r;
-      const int c = p < 16 ? p ^ L::h(r & 15) : 0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(dst + j * 1024), 16,
-                                               r * 256 + c * 16, 0, 0, 0);
-    }
-  }
-}
-
-// dma_tile by loads the compiler does not track (tiles_bf16.h, dma16): no wait for them is
-// placed before later LDS reads; the caller waits (vmcnt) before the barrier that hands the
-// tile over.
-template <class L, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile_untracked(i32x4 src, unsigned dst, int wave, int lane) {
+__device__ __forceinline__ void dma_tile(i32x4 src, unsigned dst, int wave, int lane) {
   constexpr int kInsts = ROWS * L::kSlots / 64;
   static_assert(ROWS * L::kSlots % 64 == 0, "whole DMA instructions");
 #pragma unroll
@@ -436,8 +415,8 @@ bwd_dq_kernel(BwdArgs a) {
     const int bytes = (nk - k0) * 256;
     const i32x4 kr = rsrc_words(kbase + (int64_t)k0 * kDim, bytes);
     const i32x4 vr = rsrc_words(vbase + (int64_t)k0 * kDim, bytes);
-    dma_tile_untracked<KL, kKeyTile, kQW>(kr, lds_addr(sK + buf * 2 * kKeyTile * KL::kRow), wave, lane);
-    dma_tile_untracked<KL, kKeyTile, kQW>(vr, lds_addr(sV + buf * 2 * kKeyTile * KL::kRow), wave, lane);
+    dma_tile<KL, kKeyTile, kQW>(kr, lds_addr(sK + buf * 2 * kKeyTile * KL::kRow), wave, lane);
+    dma_tile<KL, kKeyTile, kQW>(vr, lds_addr(sV + buf * 2 * kKeyTile * KL::kRow), wave, lane);
   };
   __syncthreads();   // the linear part's slabs are no longer read
   issue(0, 0);
@@ -605,8 +584,8 @@ bwd_dkdv_kernel(BwdArgs a) {
     const unsigned base = lds_addr(smem + b * kQBuf);
     const i32x4 qr = rsrc_words(reinterpret_cast<const uint16_t*>(a.q) + (hrow + r0) * kDim, bytes);
     const i32x4 yr = rsrc_words(a.dyb + (hrow + r0) * kDim, bytes);
-    dma_tile_untracked<QL, kQTile, kKW>(qr, base, wave, lane);
-    dma_tile_untracked<QL, kQTile, kKW>(yr, base + kQTile * QL::kRow, wave, lane);
+    dma_tile<QL, kQTile, kKW>(qr, base, wave, lane);
+    dma_tile<QL, kQTile, kKW>(yr, base + kQTile * QL::kRow, wave, lane);
     if (wave == 0) {
       const unsigned st = base + 2 * kQTile * QL::kRow;
       dma4(rsrc_words(a.lse + hrow + r0, bytes / 64), st, lane * 4);
