@@ -20,6 +20,8 @@
 // (Swz320, Swz256 below); the linear parts' slabs in rows of 128 bf16 padded to 272 bytes.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "tiles_bf16.h"
 
@@ -459,24 +461,31 @@ bwd_dq_kernel(BwdArgs a) {
           const unsigned char* t = bK + (32 * kb + 16 * j) * KL::kRow;
           kt[db][j] = frag_tr_at(t + KL::t_off(lane, db, 0), t + KL::t_off(lane, db, 1));
         }
+      // ds of the block; keys past nk (only in the window's last tile) are masked out
       bf16x8 dsb[2];
+      auto ds_block = [&](auto masked) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 pk;
+        for (int j = 0; j < 2; ++j) {
+          u32x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float d2[2];
+          for (int e = 0; e < 4; ++e) {
+            float d2[2];
 #pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            const int i = 8 * j + 2 * e + q2;
-            const int key = k0 + 32 * kb + cidx(i, lane);
-            const float p = key < nk ? fast_exp2(St[kb][i] * ls - lse_l) : 0.0f;
-            d2[q2] = p * (Pt[kb][i] - dd_l) * us;
+            for (int q2 = 0; q2 < 2; ++q2) {
+              const int i = 8 * j + 2 * e + q2;
+              float p = fast_exp2(St[kb][i] * ls - lse_l);
+              if (decltype(masked)::value && k0 + 32 * kb + cidx(i, lane) >= nk) p = 0.0f;
+              d2[q2] = p * (Pt[kb][i] - dd_l) * us;
+            }
+            pk[e] = pack_bf16_u32(d2[0], d2[1]);
           }
-          pk[e] = pack_bf16_u32(d2[0], d2[1]);
+          dsb[j] = as_bf16x8(pk);
         }
-        dsb[j] = as_bf16x8(pk);
-      }
+      };
+      if (F <= 128 && k0 + kKeyTile <= nk)   // (F = 256: one path, fewer registers)
+        ds_block(std::false_type{});
+      else
+        ds_block(std::true_type{});
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
