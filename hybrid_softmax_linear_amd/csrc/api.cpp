@@ -38,7 +38,8 @@ hipError_t launch_copy_rows(const void* sk, const void* sv, void* dk, void* dv, 
                             hipStream_t stream);
 hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH,
                                      int F, void* img, int64_t img_bh, int64_t img_t,
-                                     const void* W, int nW, void* wimg, hipStream_t stream);
+                                     const void* W, int nW, void* wimg, unsigned* zp, int nz,
+                                     hipStream_t stream);
 hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* params,
                                int per_head, int H, int hid, int P, int BH, int F, void* out,
                                hipStream_t stream);
@@ -437,6 +438,29 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
   const bool need_state = nch > 1;   // a single chunk has an empty linear set in both modes
   const bool bf16 = d->dtype == REHYAT_BF16;
 
+  AttnArgs a{};
+  a.q = q; a.q_rows = N; a.y = y;
+  a.ka = k; a.va = v; a.a_rows = N;
+  a.kb = k; a.vb = v; a.b_rows = N;
+  a.Wq = Wq; a.w_per_head = d->w_per_head;
+  a.S = states; a.z = states + (size_t)d->F * d->D;
+  a.s_bh = (int64_t)nch * E; a.s_t = (int64_t)E; a.z_bh = a.s_bh; a.z_t = a.s_t;
+  a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
+  a.st_img = simg; a.st_img_bh = (int64_t)(nch * image_bytes(d)); a.st_img_t = (int64_t)image_bytes(d);
+  a.phiq = (phi_ahead(d) && need_state) ? phiq : nullptr;
+  a.lse = lse;
+  a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
+  a.n_chunks = nch; a.chunk0 = 0; a.step = 0;
+  a.bidir = d->mode == REHYAT_BIDIR;
+  a.y_f32 = d->y_dtype == REHYAT_F32;
+  const int64_t Np = (int64_t)d->Tc * d->HW;
+  fill_tiles(a, d, nch, (int)(N - (int64_t)(nch - 1) * Np));
+  a.logit_scale = kLog2e / std::sqrt((float)d->D);
+  a.u_scale = us;
+  // the work counters of the persistent launch, the last kQueueBytes of the workspace: cleared
+  // by the image launch when there is one, else by a fill launch of their own
+  if (bf16 && attn_bf16_persistent(a.nblocks))
+    a.queue = reinterpret_cast<unsigned*>(reinterpret_cast<unsigned char*>(ws) + need - kQueueBytes);
   if (need_state) {
     StateArgs sa{};
     sa.ka = k; sa.va = v; sa.a_rows = N; sa.a_row0 = 0;
@@ -461,33 +485,13 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
     if (bf16) {
       e = launch_linear_images_bf16(states, (int64_t)nch * E, (int64_t)E, nch, BH, d->F, simg,
                                     (int64_t)(nch * image_bytes(d)), (int64_t)image_bytes(d), Wq,
-                                    d->w_per_head ? d->H : 1, phi_ahead(d) ? nullptr : wimg, s);
+                                    d->w_per_head ? d->H : 1, phi_ahead(d) ? nullptr : wimg,
+                                    a.queue, a.queue ? kAttnQueues : 0, s);
       if (e != hipSuccess) return hip_status(e, "linear image launch");
     }
   }
 
-  AttnArgs a{};
-  a.q = q; a.q_rows = N; a.y = y;
-  a.ka = k; a.va = v; a.a_rows = N;
-  a.kb = k; a.vb = v; a.b_rows = N;
-  a.Wq = Wq; a.w_per_head = d->w_per_head;
-  a.S = states; a.z = states + (size_t)d->F * d->D;
-  a.s_bh = (int64_t)nch * E; a.s_t = (int64_t)E; a.z_bh = a.s_bh; a.z_t = a.s_t;
-  a.wt_img = wimg; a.wt_img_head = (int64_t)image_bytes(d);
-  a.st_img = simg; a.st_img_bh = (int64_t)(nch * image_bytes(d)); a.st_img_t = (int64_t)image_bytes(d);
-  a.phiq = (phi_ahead(d) && need_state) ? phiq : nullptr;
-  a.lse = lse;
-  a.H = d->H; a.HW = d->HW; a.Tc = d->Tc; a.To = d->To; a.T = d->T;
-  a.n_chunks = nch; a.chunk0 = 0; a.step = 0;
-  a.bidir = d->mode == REHYAT_BIDIR;
-  a.y_f32 = d->y_dtype == REHYAT_F32;
-  const int64_t Np = (int64_t)d->Tc * d->HW;
-  fill_tiles(a, d, nch, (int)(N - (int64_t)(nch - 1) * Np));
-  a.logit_scale = kLog2e / std::sqrt((float)d->D);
-  a.u_scale = us;
-  if (bf16 && attn_bf16_persistent(a.nblocks)) {
-    // the work counters of the persistent launch, the last kQueueBytes of the workspace
-    a.queue = reinterpret_cast<unsigned*>(reinterpret_cast<unsigned char*>(ws) + need - kQueueBytes);
+  if (a.queue && !(need_state && bf16)) {
     hipError_t e = launch_zero_u32(a.queue, kAttnQueues, s);
     if (e != hipSuccess) return hip_status(e, "queue reset launch");
   }
@@ -602,7 +606,7 @@ rehyat_status rehyat_recurrent_step(const rehyat_desc* d, int32_t t, const void*
       hipError_t ei = launch_linear_images_bf16(S, (int64_t)d->F * d->D, 0, 1, BH, d->F, simg,
                                                 (int64_t)image_bytes(d), 0, Wq,
                                                 d->w_per_head ? d->H : 1,
-                                                phi_ahead(d) ? nullptr : wimg, s);
+                                                phi_ahead(d) ? nullptr : wimg, nullptr, 0, s);
       if (ei != hipSuccess) return hip_status(ei, "linear image launch");
       if (phi_ahead(d)) {
         ei = launch_phi_rows(d, q_c, crow, Wq, phiq_step, s);

@@ -185,11 +185,10 @@ gather_window_bf16_kernel(const uint16_t* ka, const uint16_t* va, int64_t a_rows
 //   W^T image of one W (128 x F bf16, row d): F rows f of 128 bf16; d chunk c of row f
 //     sits at chunk c ^ kappa(f mod 16).
 // st_image: one block transposes S[f0 .. f0+32)[0 .. 128) of state (t, bh) through LDS.
-__global__ void __launch_bounds__(256)
-st_image_kernel(const float* __restrict__ S, int64_t s_bh, int64_t s_t, int F,
-                unsigned char* __restrict__ img, int64_t img_bh, int64_t img_t) {
-  __shared__ float tile[32][kDim + 1];
-  const int f0 = blockIdx.x * 32, t = blockIdx.y, bh = blockIdx.z;
+__device__ __forceinline__ void st_image_block(const float* __restrict__ S, int64_t s_bh,
+                                               int64_t s_t, int F, unsigned char* __restrict__ img,
+                                               int64_t img_bh, int64_t img_t, int f0, int t,
+                                               int bh, float (*tile)[kDim + 1]) {
   const float* src = S + bh * s_bh + t * s_t + (int64_t)f0 * kDim;
   for (int i = threadIdx.x; i < 32 * kDim; i += 256) tile[i / kDim][i % kDim] = src[i];
   __syncthreads();
@@ -207,10 +206,9 @@ st_image_kernel(const float* __restrict__ S, int64_t s_bh, int64_t s_t, int F,
 }
 
 // wt_image: one block writes rows f0 .. f0+32 of the W^T image of head h.
-__global__ void __launch_bounds__(256)
-wt_image_kernel(const uint16_t* __restrict__ W, int F, unsigned char* __restrict__ img) {
-  __shared__ uint16_t tile[kDim][34];
-  const int f0 = blockIdx.x * 32, h = blockIdx.y;
+__device__ __forceinline__ void wt_image_block(const uint16_t* __restrict__ W, int F,
+                                               unsigned char* __restrict__ img, int f0, int h,
+                                               uint16_t (*tile)[34]) {
   const uint16_t* src = W + (int64_t)h * kDim * F;
   for (int i = threadIdx.x; i < kDim * 32; i += 256) {
     const int d = i >> 5, fl = i & 31;
@@ -226,6 +224,32 @@ wt_image_kernel(const uint16_t* __restrict__ W, int F, unsigned char* __restrict
       w[e] = (unsigned)tile[8 * c + 2 * e][fl] | ((unsigned)tile[8 * c + 2 * e + 1][fl] << 16);
     *reinterpret_cast<u32x4*>(dst + f * 256 + ((c ^ kappa(f & 15)) << 4)) = w;
   }
+}
+
+// One launch for both images and, optionally, the clearing of nz words at zp (the work
+// counters of the attention launch that follows on the same stream): blocks
+// [0, n_st) are S^T image blocks (f block fastest, then state t, then bh), the next n_wt
+// W^T image blocks (f block fastest, then h), and one last block clears zp when nz > 0.
+__global__ void __launch_bounds__(256)
+linear_images_kernel(const float* __restrict__ S, int64_t s_bh, int64_t s_t, int nst, int F,
+                     unsigned char* __restrict__ img, int64_t img_bh, int64_t img_t,
+                     const uint16_t* __restrict__ W, unsigned char* __restrict__ wimg, int n_st,
+                     int n_wt, unsigned* __restrict__ zp, int nz) {
+  __shared__ __attribute__((aligned(16))) float tile[32 * (kDim + 1)];
+  const int nfb = F / 32;
+  int b = blockIdx.x;
+  if (b < n_st) {
+    const int fb = b % nfb, r = b / nfb;
+    st_image_block(S, s_bh, s_t, F, img, img_bh, img_t, 32 * fb, r % nst, r / nst,
+                   reinterpret_cast<float (*)[kDim + 1]>(tile));
+    return;
+  }
+  b -= n_st;
+  if (b < n_wt) {
+    wt_image_block(W, F, wimg, 32 * (b % nfb), b / nfb, reinterpret_cast<uint16_t (*)[34]>(tile));
+    return;
+  }
+  for (int i = threadIdx.x; i < nz; i += 256) zp[i] = 0u;
 }
 
 // Per-segment partial states from phi(k) rows computed ahead (feature maps other than
@@ -633,21 +657,20 @@ hipError_t launch_phi_bf16(const void* x, int64_t n, const void* W, int w_per_he
 
 // S^T images of nst states per head (state (bh, t) at S + bh*s_bh + t*s_t, [F][128] fp32)
 // into img + bh*img_bh + t*img_t, and the W^T image of each of nW matrices W ([nW][128][F]
-// bf16) into wimg + h*F*256 (wimg may be null to skip it).
+// bf16) into wimg + h*F*256 (wimg may be null to skip it), in one launch; with nz > 0 the
+// same launch also clears the nz 32-bit words at zp.
 hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH,
                                      int F, void* img, int64_t img_bh, int64_t img_t,
-                                     const void* W, int nW, void* wimg, hipStream_t stream) {
-  if (F % 32 != 0) return hipErrorInvalidValue;
-  if (nst > 0) {
-    dim3 grid(F / 32, nst, BH), block(256);
-    hipLaunchKernelGGL(st_image_kernel, grid, block, 0, stream, S, s_bh, s_t, F,
-                       (unsigned char*)img, img_bh, img_t);
-  }
-  if (wimg) {
-    dim3 grid(F / 32, nW), block(256);
-    hipLaunchKernelGGL(wt_image_kernel, grid, block, 0, stream, (const uint16_t*)W, F,
-                       (unsigned char*)wimg);
-  }
+                                     const void* W, int nW, void* wimg, unsigned* zp, int nz,
+                                     hipStream_t stream) {
+  if (F % 32 != 0 || nz < 0 || (nz > 0 && !zp)) return hipErrorInvalidValue;
+  const int n_st = nst > 0 ? (F / 32) * nst * BH : 0;
+  const int n_wt = wimg ? (F / 32) * nW : 0;
+  const int nblk = n_st + n_wt + (nz > 0 ? 1 : 0);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(linear_images_kernel, dim3(nblk), dim3(256), 0, stream, S, s_bh, s_t, nst,
+                     F, (unsigned char*)img, img_bh, img_t, (const uint16_t*)W,
+                     (unsigned char*)wimg, n_st, n_wt, zp, nz);
   return hipGetLastError();
 }
 
