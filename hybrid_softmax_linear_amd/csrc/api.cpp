@@ -26,7 +26,9 @@ hipError_t launch_phi_bf16(const void* x, int64_t n, const void* W, int w_per_he
 hipError_t launch_phi_f32(const void* x, int64_t n, const void* W, int w_per_head, int H, int BH,
                           int D, int F, void* out, float u_scale, hipStream_t stream);
 hipError_t launch_scan_states(const float* part, float* states, int F, int D, int T, int Tc,
-                              int To, int nch, int bidir, int BH, hipStream_t stream);
+                              int To, int nch, int bidir, int BH, void* img, int64_t img_bh,
+                              int64_t img_t, const void* W, int nW, void* wimg, unsigned* zp,
+                              int nz, hipStream_t stream);
 hipError_t launch_fold_states(const float* part, int nseg, float* S, float* z, int F, int D,
                               int init, int BH, hipStream_t stream);
 hipError_t launch_gather_window_bf16(const void* ka, const void* va, int64_t a_rows, int64_t a_row0,
@@ -458,7 +460,7 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
   a.logit_scale = kLog2e / std::sqrt((float)d->D);
   a.u_scale = us;
   // the work counters of the persistent launch, the last kQueueBytes of the workspace: cleared
-  // by the image launch when there is one, else by a fill launch of their own
+  // by the state scan's launch when there is one, else by a fill launch of their own
   if (bf16 && attn_bf16_persistent(a.nblocks))
     a.queue = reinterpret_cast<unsigned*>(reinterpret_cast<unsigned char*>(ws) + need - kQueueBytes);
   if (need_state) {
@@ -479,19 +481,16 @@ rehyat_status hybrid_fwd_impl(const rehyat_desc* d, const void* q, const void* k
     }
     hipError_t e = launch_partial(d, sa, s);
     if (e != hipSuccess) return hip_status(e, "state partial launch");
+    // the scan also writes the bf16 images of the linear branch and clears the counters
     e = launch_scan_states(part, states, d->F, d->D, d->T, d->Tc, d->To, nch,
-                           d->mode == REHYAT_BIDIR, BH, s);
+                           d->mode == REHYAT_BIDIR, BH, bf16 ? simg : nullptr,
+                           (int64_t)(nch * image_bytes(d)), (int64_t)image_bytes(d), Wq,
+                           d->w_per_head ? d->H : 1, (bf16 && !phi_ahead(d)) ? wimg : nullptr,
+                           a.queue, a.queue ? kAttnQueues : 0, s);
     if (e != hipSuccess) return hip_status(e, "state scan launch");
-    if (bf16) {
-      e = launch_linear_images_bf16(states, (int64_t)nch * E, (int64_t)E, nch, BH, d->F, simg,
-                                    (int64_t)(nch * image_bytes(d)), (int64_t)image_bytes(d), Wq,
-                                    d->w_per_head ? d->H : 1, phi_ahead(d) ? nullptr : wimg,
-                                    a.queue, a.queue ? kAttnQueues : 0, s);
-      if (e != hipSuccess) return hip_status(e, "linear image launch");
-    }
   }
 
-  if (a.queue && !(need_state && bf16)) {
+  if (a.queue && !need_state) {
     hipError_t e = launch_zero_u32(a.queue, kAttnQueues, s);
     if (e != hipSuccess) return hip_status(e, "queue reset launch");
   }
@@ -930,7 +929,9 @@ rehyat_status rehyat_hybrid_bwd(const rehyat_desc* d, const void* q, const void*
     sa.Wk = Wk; sa.w_per_head = d->w_per_head; sa.H = d->H;
     sa.part = part; sa.u_scale = us;
     REHYAT_TRY(launch_partial(d, sa, s), "state partial launch");
-    REHYAT_TRY(launch_scan_states(part, states, F, D, T, d->Tc, d->To, nch, 0, BH, s), "state scan launch");
+    REHYAT_TRY(launch_scan_states(part, states, F, D, T, d->Tc, d->To, nch, 0, BH, nullptr, 0, 0,
+                                  nullptr, 0, nullptr, nullptr, 0, s),
+               "state scan launch");
     REHYAT_TRY(launch_state_rows_bf16(states, nch * E, E, nch, BH, F, simg, s), "state image launch");
   }
   REHYAT_TRY(launch_transpose_w(Wq, F, nW, wtq, s), "transpose launch");

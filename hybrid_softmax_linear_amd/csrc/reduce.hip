@@ -1,43 +1,16 @@
 // reduce.hip - fp32 combination of partial states and the overlap-tail copy.
 //
 // Partial states are [BH][segments][E] with E = F*D + F (S row-major, then z).
-//   scan: per-frame partials -> the linear-branch state of every chunk of the sequence:
-//         causal        S_t = sum of frames [0, lo_t/HW)                  (key design 4)
-//         bidirectional S_t = frames [0, lo_t/HW) + frames [hi_t/HW, T)   (key design 1,
-//                       the complement of the overlapped window)
-//   fold: S = (init ? 0 : S) + sum of segments (the state update of the chunk-wise RNN).
+//   fold: S = (init ? 0 : S) + sum of segments (the state update of the chunk-wise RNN,
+//         papernotes.org ReHyAt note, key design 4).
+// (The scan of the whole-sequence form, which also writes the attention kernel's bf16
+// state images, is in state_bf16.hip.)
 // Sums run in a fixed order: results are bitwise reproducible.
 #include "common.h"
 
 namespace rehyat {
 
 namespace {
-
-__global__ void __launch_bounds__(256)
-scan_states_kernel(const float* __restrict__ part, float* __restrict__ states, int E, int T,
-                   int Tc, int To, int nch, int bidir) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int bh = blockIdx.y;
-  if (e >= E) return;
-  const float* p = part + (int64_t)bh * T * E + e;
-  float* s = states + (int64_t)bh * nch * E + e;
-  float acc = 0.0f;
-  int f = 0;
-  for (int t = 0; t < nch; ++t) {
-    const int lof = (t * Tc - To) > 0 ? (t * Tc - To) : 0;
-    for (; f < lof; ++f) acc += p[(int64_t)f * E];
-    s[(int64_t)t * E] = acc;
-  }
-  if (bidir) {
-    acc = 0.0f;
-    f = T - 1;
-    for (int t = nch - 1; t >= 0; --t) {
-      const int hif = ((t + 1) * Tc < T) ? (t + 1) * Tc : T;
-      for (; f >= hif; --f) acc += p[(int64_t)f * E];
-      s[(int64_t)t * E] += acc;
-    }
-  }
-}
 
 __global__ void __launch_bounds__(256)
 fold_states_kernel(const float* __restrict__ part, int nseg, float* S, float* z, int F, int D,
@@ -76,14 +49,6 @@ __global__ void __launch_bounds__(64) zero_u32_kernel(unsigned* p, int n) {
 // Zero n 32-bit words (a fill kernel: callers may capture it in a graph).
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream) {
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_scan_states(const float* part, float* states, int F, int D, int T, int Tc,
-                              int To, int nch, int bidir, int BH, hipStream_t stream) {
-  const int E = F * D + F;
-  dim3 grid((E + 255) / 256, BH), block(256);
-  hipLaunchKernelGGL(scan_states_kernel, grid, block, 0, stream, part, states, E, T, Tc, To, nch, bidir);
   return hipGetLastError();
 }
 

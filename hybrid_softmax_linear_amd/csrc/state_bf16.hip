@@ -226,6 +226,86 @@ __device__ __forceinline__ void wt_image_block(const uint16_t* __restrict__ W, i
   }
 }
 
+// Per-chunk states from the frame partials part [BH][T][E] (E = F*D + F: S row-major, then
+// z) into states [BH][nch][E], each element summed in frame order (papernotes.org ReHyAt
+// note, key designs 1 and 4):
+//   causal        S_t = frames [0, lo_t/HW)
+//   bidirectional S_t = frames [0, lo_t/HW) + frames [hi_t/HW, T) (the complement of the
+//                 window)
+// Block (bh, 8 features, 32 d): thread (f, d) sums element f*D + d, the d = 0 threads also
+// z[f]. With img set (D = 128) the block also writes the bf16 S^T image of every state it
+// finishes (8 features of 32 rows d: one 16-byte chunk per row, through LDS), the layout of
+// st_image_block. Blocks from n_scan on are the W^T image blocks and the counter-clearing
+// block of linear_images_kernel (n_wt, nz as there).
+__global__ void __launch_bounds__(256)
+scan_states_kernel(const float* __restrict__ part, float* __restrict__ states, int F, int D, int T,
+                   int Tc, int To, int nch, int bidir, int n_scan, unsigned char* __restrict__ img,
+                   int64_t img_bh, int64_t img_t, const uint16_t* __restrict__ W,
+                   unsigned char* __restrict__ wimg, int n_wt, unsigned* __restrict__ zp, int nz) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kDim][34];
+  int b = blockIdx.x;
+  if (b >= n_scan) {
+    b -= n_scan;
+    if (b < n_wt) wt_image_block(W, F, wimg, 32 * (b % (F / 32)), b / (F / 32), tile);
+    else for (int i = threadIdx.x; i < nz; i += 256) zp[i] = 0u;
+    return;
+  }
+  float (*st)[32] = reinterpret_cast<float (*)[32]>(&tile[0][0]);   // [8 f][32 d]
+  const int ndb = D / 32, nfb = F / 8;
+  const int db = b % ndb, fb = (b / ndb) % nfb, bh = b / (ndb * nfb);
+  const int fl = threadIdx.x >> 5, dl = threadIdx.x & 31;
+  const int f = 8 * fb + fl, d = 32 * db + dl;
+  const int64_t E = (int64_t)F * D + F;
+  const int64_t ei = (int64_t)f * D + d, ez = (int64_t)F * D + f;
+  const bool zl = db == 0 && dl == 0;
+  const float* p = part + (int64_t)bh * T * E;
+  float* s = states + (int64_t)bh * nch * E;
+  // bf16 image of state t's 8 x 32 block
+  auto image = [&](int t, float x) {
+    st[fl][dl] = x;
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int FS = F < 128 ? F : 128, NCH = FS / 8;
+      const int f0 = 8 * fb, dd = 32 * db + threadIdx.x;
+      const int c = (f0 % FS) >> 3;
+      unsigned char* dst = img + bh * img_bh + t * img_t + (int64_t)(f0 / FS) * kDim * FS * 2;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16_u32(st[2 * e][threadIdx.x], st[2 * e + 1][threadIdx.x]);
+      *reinterpret_cast<u32x4*>(dst + dd * FS * 2 + ((c ^ (dd & (NCH - 1))) << 4)) = w;
+    }
+    __syncthreads();
+  };
+  float acc = 0.0f, accz = 0.0f;
+  int fr = 0;
+  for (int t = 0; t < nch; ++t) {
+    const int lof = (t * Tc - To) > 0 ? (t * Tc - To) : 0;
+    for (; fr < lof; ++fr) {
+      acc += p[fr * E + ei];
+      if (zl) accz += p[fr * E + ez];
+    }
+    s[t * E + ei] = acc;
+    if (zl) s[t * E + ez] = accz;
+    if (img && !bidir) image(t, acc);
+  }
+  if (bidir) {
+    acc = 0.0f;
+    accz = 0.0f;
+    fr = T - 1;
+    for (int t = nch - 1; t >= 0; --t) {
+      const int hif = ((t + 1) * Tc < T) ? (t + 1) * Tc : T;
+      for (; fr >= hif; --fr) {
+        acc += p[fr * E + ei];
+        if (zl) accz += p[fr * E + ez];
+      }
+      const float x = s[t * E + ei] + acc;
+      s[t * E + ei] = x;
+      if (zl) s[t * E + ez] += accz;
+      if (img) image(t, x);
+    }
+  }
+}
+
 // One launch for both images and, optionally, the clearing of nz words at zp (the work
 // counters of the attention launch that follows on the same stream): blocks
 // [0, n_st) are S^T image blocks (f block fastest, then state t, then bh), the next n_wt
@@ -671,6 +751,25 @@ hipError_t launch_linear_images_bf16(const float* S, int64_t s_bh, int64_t s_t, 
   hipLaunchKernelGGL(linear_images_kernel, dim3(nblk), dim3(256), 0, stream, S, s_bh, s_t, nst,
                      F, (unsigned char*)img, img_bh, img_t, (const uint16_t*)W,
                      (unsigned char*)wimg, n_st, n_wt, zp, nz);
+  return hipGetLastError();
+}
+
+// The per-chunk states (scan_states_kernel); with img set (bf16, D = 128) also their S^T
+// images, and in the same launch the W^T images of wimg (if set) and the clearing of nz
+// words at zp.
+hipError_t launch_scan_states(const float* part, float* states, int F, int D, int T, int Tc,
+                              int To, int nch, int bidir, int BH, void* img, int64_t img_bh,
+                              int64_t img_t, const void* W, int nW, void* wimg, unsigned* zp,
+                              int nz, hipStream_t stream) {
+  if (F % 8 != 0 || D % 32 != 0 || ((img || wimg) && (F % 32 != 0 || D != kDim)) || nz < 0 ||
+      (nz > 0 && !zp))
+    return hipErrorInvalidValue;
+  const int n_scan = BH * (F / 8) * (D / 32);
+  const int n_wt = wimg ? (F / 32) * nW : 0;
+  const int nblk = n_scan + n_wt + (nz > 0 ? 1 : 0);
+  hipLaunchKernelGGL(scan_states_kernel, dim3(nblk), dim3(256), 0, stream, part, states, F, D, T,
+                     Tc, To, nch, bidir, n_scan, (unsigned char*)img, img_bh, img_t,
+                     (const uint16_t*)W, (unsigned char*)wimg, n_wt, zp, nz);
   return hipGetLastError();
 }
 
