@@ -201,7 +201,7 @@ def bench_bwd(args):
 def bench_stream(args):
     """One line for streaming: 27 recurrent steps over the 81x30x52 latent (B1 H12, Tc3 To1),
     each step's q, k, v chunk resident in HBM; a pass is the 27 steps, each one launch of
-    rehyat_recurrent_step_fused. Context: the same pass with rehyat_recurrent_step (seven
+    rehyat_recurrent_step_fused. Context: the same pass with rehyat_recurrent_step (six
     launches per step), and the pass with each chunk copied from pinned host memory before
     its step (PCIe-inclusive; the copies alone are timed too)."""
     import torch
