@@ -226,20 +226,47 @@ __device__ __forceinline__ void wt_image_block(const uint16_t* __restrict__ W, i
   }
 }
 
+// The scan of one element (p: its frame-0 partial, frames E apart; s: its chunk-0 state,
+// chunks E apart), as scan_states_kernel's blocks do it.
+__device__ __forceinline__ void scan_one(const float* __restrict__ p, float* __restrict__ s,
+                                         int64_t E, int T, int Tc, int To, int nch, int bidir) {
+  float acc = 0.0f;
+  int fr = 0;
+  for (int t = 0; t < nch; ++t) {
+    const int lof = (t * Tc - To) > 0 ? (t * Tc - To) : 0;
+#pragma unroll 4
+    for (; fr < lof; ++fr) acc += p[fr * E];
+    s[t * E] = acc;
+  }
+  if (bidir) {
+    acc = 0.0f;
+    fr = T - 1;
+    for (int t = nch - 1; t >= 0; --t) {
+      const int hif = ((t + 1) * Tc < T) ? (t + 1) * Tc : T;
+#pragma unroll 4
+      for (; fr >= hif; --fr) acc += p[fr * E];
+      s[t * E] += acc;
+    }
+  }
+}
+
 // Per-chunk states from the frame partials part [BH][T][E] (E = F*D + F: S row-major, then
 // z) into states [BH][nch][E], each element summed in frame order (papernotes.org ReHyAt
 // note, key designs 1 and 4):
 //   causal        S_t = frames [0, lo_t/HW)
 //   bidirectional S_t = frames [0, lo_t/HW) + frames [hi_t/HW, T) (the complement of the
 //                 window)
-// Block (bh, 8 features, 32 d): thread (f, d) sums element f*D + d, the d = 0 threads also
-// z[f]. With img set (D = 128) the block also writes the bf16 S^T image of every state it
-// finishes (8 features of 32 rows d: one 16-byte chunk per row, through LDS), the layout of
-// st_image_block. Blocks from n_scan on are the W^T image blocks and the counter-clearing
-// block of linear_images_kernel (n_wt, nz as there).
+// Blocks [0, n_s): (bh, 8 features, 32 d), thread (f, d) sums element f*D + d; with img set
+// (D = 128) the block also writes the bf16 S^T image of every state it finishes (8 features
+// of 32 rows d: one 16-byte chunk per row, through LDS), the layout of st_image_block.
+// Blocks [n_s, n_scan): the z elements, one per thread (kept out of the S blocks so that
+// their frame loop has no branch and keeps several frames' loads in flight). Blocks from
+// n_scan on are the W^T image blocks and the counter-clearing block of linear_images_kernel
+// (n_wt, nz as there).
 __global__ void __launch_bounds__(256)
 scan_states_kernel(const float* __restrict__ part, float* __restrict__ states, int F, int D, int T,
-                   int Tc, int To, int nch, int bidir, int n_scan, unsigned char* __restrict__ img,
+                   int Tc, int To, int nch, int bidir, int n_s, int n_scan,
+                   unsigned char* __restrict__ img,
                    int64_t img_bh, int64_t img_t, const uint16_t* __restrict__ W,
                    unsigned char* __restrict__ wimg, int n_wt, unsigned* __restrict__ zp, int nz) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kDim][34];
@@ -250,16 +277,25 @@ scan_states_kernel(const float* __restrict__ part, float* __restrict__ states, i
     else for (int i = threadIdx.x; i < nz; i += 256) zp[i] = 0u;
     return;
   }
+  const int64_t E = (int64_t)F * D + F;
+  if (b >= n_s) {
+    // z: one element per thread, no image
+    b -= n_s;
+    const int nzb = (F + 255) / 256;
+    const int bh = b / nzb, f = (b % nzb) * 256 + threadIdx.x;
+    if (f >= F) return;
+    const float* p = part + (int64_t)bh * T * E + (int64_t)F * D + f;
+    float* s = states + (int64_t)bh * nch * E + (int64_t)F * D + f;
+    scan_one(p, s, E, T, Tc, To, nch, bidir);
+    return;
+  }
   float (*st)[32] = reinterpret_cast<float (*)[32]>(&tile[0][0]);   // [8 f][32 d]
   const int ndb = D / 32, nfb = F / 8;
   const int db = b % ndb, fb = (b / ndb) % nfb, bh = b / (ndb * nfb);
   const int fl = threadIdx.x >> 5, dl = threadIdx.x & 31;
   const int f = 8 * fb + fl, d = 32 * db + dl;
-  const int64_t E = (int64_t)F * D + F;
-  const int64_t ei = (int64_t)f * D + d, ez = (int64_t)F * D + f;
-  const bool zl = db == 0 && dl == 0;
-  const float* p = part + (int64_t)bh * T * E;
-  float* s = states + (int64_t)bh * nch * E;
+  const float* p = part + (int64_t)bh * T * E + (int64_t)f * D + d;
+  float* s = states + (int64_t)bh * nch * E + (int64_t)f * D + d;
   // bf16 image of state t's 8 x 32 block
   auto image = [&](int t, float x) {
     st[fl][dl] = x;
@@ -276,31 +312,24 @@ scan_states_kernel(const float* __restrict__ part, float* __restrict__ states, i
     }
     __syncthreads();
   };
-  float acc = 0.0f, accz = 0.0f;
+  float acc = 0.0f;
   int fr = 0;
   for (int t = 0; t < nch; ++t) {
     const int lof = (t * Tc - To) > 0 ? (t * Tc - To) : 0;
-    for (; fr < lof; ++fr) {
-      acc += p[fr * E + ei];
-      if (zl) accz += p[fr * E + ez];
-    }
-    s[t * E + ei] = acc;
-    if (zl) s[t * E + ez] = accz;
+#pragma unroll 4
+    for (; fr < lof; ++fr) acc += p[fr * E];
+    s[t * E] = acc;
     if (img && !bidir) image(t, acc);
   }
   if (bidir) {
     acc = 0.0f;
-    accz = 0.0f;
     fr = T - 1;
     for (int t = nch - 1; t >= 0; --t) {
       const int hif = ((t + 1) * Tc < T) ? (t + 1) * Tc : T;
-      for (; fr >= hif; --fr) {
-        acc += p[fr * E + ei];
-        if (zl) accz += p[fr * E + ez];
-      }
-      const float x = s[t * E + ei] + acc;
-      s[t * E + ei] = x;
-      if (zl) s[t * E + ez] += accz;
+#pragma unroll 4
+      for (; fr >= hif; --fr) acc += p[fr * E];
+      const float x = s[t * E] + acc;
+      s[t * E] = x;
       if (img) image(t, x);
     }
   }
@@ -764,11 +793,12 @@ hipError_t launch_scan_states(const float* part, float* states, int F, int D, in
   if (F % 8 != 0 || D % 32 != 0 || ((img || wimg) && (F % 32 != 0 || D != kDim)) || nz < 0 ||
       (nz > 0 && !zp))
     return hipErrorInvalidValue;
-  const int n_scan = BH * (F / 8) * (D / 32);
+  const int n_s = BH * (F / 8) * (D / 32);
+  const int n_scan = n_s + BH * ((F + 255) / 256);
   const int n_wt = wimg ? (F / 32) * nW : 0;
   const int nblk = n_scan + n_wt + (nz > 0 ? 1 : 0);
   hipLaunchKernelGGL(scan_states_kernel, dim3(nblk), dim3(256), 0, stream, part, states, F, D, T,
-                     Tc, To, nch, bidir, n_scan, (unsigned char*)img, img_bh, img_t,
+                     Tc, To, nch, bidir, n_s, n_scan, (unsigned char*)img, img_bh, img_t,
                      (const uint16_t*)W, (unsigned char*)wimg, n_wt, zp, nz);
   return hipGetLastError();
 }
