@@ -309,6 +309,7 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
   for (int f = tid; f < F; f += NT) zs[f] = z[f];
   constexpr int FS = F < 128 ? F : 128;   // features per LDS slab
   constexpr int NFB = FS / 32;            // 32-feature blocks per slab
+  const float c1 = a.u_scale, c2 = 0.5f * a.u_scale * a.u_scale;
   constexpr int NCH = FS / 8;             // 16-byte chunks per S^T row
   constexpr int SLAB = FS * 256;          // bytes of one W^T slab and of one S^T slab
   const unsigned char* wimg = reinterpret_cast<const unsigned char*>(a.wt_img) +
@@ -385,7 +386,8 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
           }
           U[k] = mfma32(av, Q.op[s], U[k]);
         }
-      // phi = 1 + u + u^2/2, rounded to bf16: B operand of a^L^T = S^T phi^T.
+      // phi = 1 + u + u^2/2 with u = U / sqrt(D), as 1 + U (c1 + c2 U) (c1 = 1/sqrt(D),
+      // c2 = c1^2 / 2), rounded to bf16: B operand of a^L^T = S^T phi^T; n^L takes phi in fp32
 #pragma unroll
       for (int k = 0; k < G; ++k)
 #pragma unroll
@@ -394,13 +396,12 @@ __device__ __forceinline__ void linear_branch(Acc& A, float& nlf, const AttnArgs
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i0 = 8 * j + 2 * e;
-            float u0 = U[k][i0] * a.u_scale, u1 = U[k][i0 + 1] * a.u_scale;
-            float p0 = 1.0f + u0 + 0.5f * u0 * u0;
-            float p1 = 1.0f + u1 + 0.5f * u1 * u1;
-            unsigned w = pack_bf16_u32(p0, p1);
-            pk[e] = w;
+            const float p0 = fmaf(U[k][i0], fmaf(U[k][i0], c2, c1), 1.0f);
+            const float p1 = fmaf(U[k][i0 + 1], fmaf(U[k][i0 + 1], c2, c1), 1.0f);
+            pk[e] = pack_bf16_u32(p0, p1);
             const int f = f0 + 32 * (fg + k) + cidx(i0, lane);
-            nl += bf16_lo(w) * zs[f] + bf16_hi(w) * zs[f + 1];
+            nl = fmaf(p0, zs[f], nl);
+            nl = fmaf(p1, zs[f + 1], nl);
           }
           P[k][j] = as_bf16x8(pk);
         }
