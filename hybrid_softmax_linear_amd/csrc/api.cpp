@@ -47,7 +47,7 @@ hipError_t launch_phi_map_bf16(int kind, const void* x, int64_t n, const void* p
                                hipStream_t stream);
 hipError_t launch_state_partial_phi_bf16(const StateArgs& a, int F, int BH, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* y, const void* dy, int y_f32, const float* lse, int64_t rows,
-                           uint16_t* dyb, uint16_t* gb, float* cvec, float* dvec,
+                           float us, uint16_t* dyb, uint16_t* gb, float* cvec, float* dvec,
                            hipStream_t stream);
 hipError_t launch_state_rows_bf16(const float* S, int64_t s_bh, int64_t s_t, int nst, int BH, int F,
                                   uint16_t* img, hipStream_t stream);
@@ -937,7 +937,7 @@ rehyat_status rehyat_hybrid_bwd(const rehyat_desc* d, const void* q, const void*
   REHYAT_TRY(launch_transpose_w(Wq, F, nW, wtq, s), "transpose launch");
   REHYAT_TRY(launch_transpose_w(Wk, F, nW, wtk, s), "transpose launch");
   // 2. per-row dy.y, dy / den
-  REHYAT_TRY(launch_bwd_prep(y, dy, d->y_dtype == REHYAT_F32, lse, (int64_t)BH * N, dyb, gb, cvec, dvec, s),
+  REHYAT_TRY(launch_bwd_prep(y, dy, d->y_dtype == REHYAT_F32, lse, (int64_t)BH * N, us, dyb, gb, cvec, dvec, s),
              "prep launch");
   // 3. dq (window and linear read-out), phi(q) and gq rows
   BwdArgs a{};

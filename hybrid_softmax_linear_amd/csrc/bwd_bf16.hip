@@ -123,9 +123,11 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, int rb, const uin
 
 // ---- per-row preparation ----------------------------------------------------------------
 // 16 lanes per row (8 elements each): dy.y, 2^-lse, and the bf16 rows of dy and dy / den.
+// dvec holds (dy.y) / sqrt(D) (us = 1/sqrt(D)), the form in which the window parts use it:
+// ds = p (dP - dy.y) / sqrt(D) = p * fma(dP, us, -dvec).
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const void* __restrict__ y, const void* __restrict__ dy, int y_f32,
-                const float* __restrict__ lse, int64_t rows, uint16_t* __restrict__ dyb,
+                const float* __restrict__ lse, int64_t rows, float us, uint16_t* __restrict__ dyb,
                 uint16_t* __restrict__ gb, float* __restrict__ cvec, float* __restrict__ dvec) {
   const int tid = threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
@@ -175,7 +177,7 @@ bwd_prep_kernel(const void* __restrict__ y, const void* __restrict__ dy, int y_f
   *reinterpret_cast<u32x4*>(gb + row * kDim + 8 * c) = pg;
   if (c == 0) {
     cvec[row] = dot * inv;
-    dvec[row] = dot;
+    dvec[row] = dot * us;
   }
 }
 
@@ -475,7 +477,7 @@ bwd_dq_kernel(BwdArgs a) {
               const int i = 8 * j + 2 * e + q2;
               float p = fast_exp2(St[kb][i] * ls - lse_l);
               if (decltype(masked)::value && k0 + 32 * kb + cidx(i, lane) >= nk) p = 0.0f;
-              d2[q2] = p * (Pt[kb][i] - dd_l) * us;
+              d2[q2] = p * fmaf(Pt[kb][i], us, -dd_l);
             }
             pk[e] = pack_bf16_u32(d2[0], d2[1]);
           }
@@ -659,7 +661,7 @@ bwd_dkdv_kernel(BwdArgs a) {
           const float Dv = Dq[2 * j + (2 * e + q2) / 4][(2 * e + q2) % 4];
           const float p = key_in ? fast_exp2(S[i] * ls - Lv) : 0.0f;
           p2[q2] = p;
-          d2[q2] = p * (Pd[i] - Dv) * us;
+          d2[q2] = p * fmaf(Pd[i], us, -Dv);
         }
         pp[e] = pack_bf16_u32(p2[0], p2[1]);
         pd[e] = pack_bf16_u32(d2[0], d2[1]);
@@ -795,10 +797,10 @@ bwd_dkdv_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_bwd_prep(const void* y, const void* dy, int y_f32, const float* lse, int64_t rows,
-                           uint16_t* dyb, uint16_t* gb, float* cvec, float* dvec,
+                           float us, uint16_t* dyb, uint16_t* gb, float* cvec, float* dvec,
                            hipStream_t stream) {
   dim3 grid((unsigned)((rows + 15) / 16)), block(256);
-  hipLaunchKernelGGL(bwd_prep_kernel, grid, block, 0, stream, y, dy, y_f32, lse, rows, dyb, gb,
+  hipLaunchKernelGGL(bwd_prep_kernel, grid, block, 0, stream, y, dy, y_f32, lse, rows, us, dyb, gb,
                      cvec, dvec);
   return hipGetLastError();
 }

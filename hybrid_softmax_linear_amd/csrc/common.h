@@ -174,7 +174,7 @@ struct BwdArgs {
   const uint16_t* gb;       // dy / den rounded to bf16 (den = the row's joint normaliser)
   const float* lse;         // [BH][N] log2(den)
   const float* cvec;        // [BH][N] (dy . y) / den
-  const float* dvec;        // [BH][N] dy . y
+  const float* dvec;        // [BH][N] (dy . y) / sqrt(D)
   const uint16_t* w;        // the map's W [nW][128][F] (q side in the dq kernel, k side in dkdv)
   const uint16_t* wt;       // its transpose [nW][F][128]
   int w_per_head;
