@@ -5,8 +5,8 @@ H12 with per-head scales), causal form, bf16 inputs, fp32 output, in the launch
 configuration bench.py --sweep times. To > Tc (a window reaching further back than one
 chunk) is part of the grid.
 
-Sampled query rows (first and last rows of every chunk plus random rows) of three heads
-per grid point are checked against the float64 oracle with the same bars as the other
+Sampled query rows (first and last rows of every chunk plus random rows) of three or four
+heads per grid point are checked against the float64 oracle with the same bars as the other
 bf16 tests.
 """
 import numpy as np
@@ -22,9 +22,11 @@ DEV = "cuda"
 GRID = [(tc, to) for tc in (1, 2, 3, 5, 7) for to in (0, 1, 2, 3)]
 
 
-# the two latents; heads checked per grid point
+# the two latents; (batch item, head) pairs checked per grid point. At 21x30x52 head 2 has
+# the largest per-head scale of the seeded draw (logit standard deviation about 4.4), the
+# case where rounding of the logits weighs most.
 LATENTS = {"21x20x30": (2, [(0, 0), (0, 5), (0, 11)]),
-           "21x30x52": (3, [(0, 0), (1, 6), (1, 11)])}
+           "21x30x52": (3, [(0, 0), (0, 2), (1, 6), (1, 11)])}
 
 
 @pytest.fixture(scope="module", params=sorted(LATENTS))
